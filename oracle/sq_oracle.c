@@ -1,0 +1,206 @@
+/*
+ * sq_oracle.c -- plain, slow CPU reference of the SmoothQuant W8A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or run
+ * this file; only the tests, the smoke check and the benchmark's CPU baseline
+ * use it.  It shares no code, header or constant with the HIP library.
+ *
+ * Every step is the plain definition, written with ordinary loops, in the order
+ * the pages give it.  Floating point is IEEE binary32 wherever the layer's
+ * contract fixes fp32 (scales, smoothed values, the dequantised output); the
+ * smoothing factor is evaluated in binary64 and rounded once.  Build with
+ *   gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp
+ * so that each C operator is exactly one correctly rounded IEEE operation.
+ *
+ * Sources (pages as they are titled; sections / equations named):
+ *   [P2] multigrid.ai "SmoothQuant Explained", section "Alpha: how much
+ *        difficulty to move" (the s_j formula and its alpha = 0 / 1 forms).
+ *   [P3] inferenceinterviews.com "Why do activation outliers break INT8 W8A8 on
+ *        LLMs...", section "A strong answer" (the identity
+ *        XW^T = (X diag(s)^-1)(W diag(s))^T, the s_j formula with max over
+ *        tokens t and output rows n, per-token and per-output-channel scales
+ *        applied in the epilogue).
+ *   [P4] mercemay.com "Activation Outlier Channels and Mixed-Precision
+ *        Decomposition", section "Decomposition" (integer matmul followed by a
+ *        float epilogue that multiplies by the product of the two scales).
+ *   [P5] maitreyasuin.github.io "...01-one-outlier", sections "The four
+ *        operations" (q = clamp(round(x/s), -n, n), scale = limit/n, n = 127,
+ *        round then clamp, the all-zero case gives codes 0 and scale 1),
+ *        "Which scales factor out, and why" (Y_tn = sum_k X_tk W_nk with
+ *        W_nk = s_n Q_nk and X_tk = a_t P_tk) and "Route it, or move it"
+ *        (maxima clamped below at 1e-8 before the powers).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define SQO_N 127        /* [P5] n = 2^(bits-1) - 1 for 8 bits                 */
+#define SQO_EPS 1e-8f    /* [P5] "Route it, or move it": clamp_min(eps) on maxima */
+
+/* Column absolute maximum: out[j] = max_i |A[i][j]|.  [P3] max_t |X_tj| and
+ * max_n |W_nj|; [P5] amax over dim 0 of act and of the weights. */
+void sqo_col_absmax(const float *A, int64_t rows, int64_t cols, float *out)
+{
+    for (int64_t j = 0; j < cols; ++j) out[j] = 0.0f;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) {
+            float a = fabsf(A[i * cols + j]);
+            if (a > out[j]) out[j] = a;
+        }
+}
+
+/* Smoothing factor.  [P2]/[P3]: s_j = max|X_j|^alpha / max|W_j|^(1-alpha);
+ * [P5]: both maxima clamped below at 1e-8 first.  Evaluated in binary64 and
+ * rounded once to binary32.  pow(x, 0) = 1 and pow(x, 1) = x exactly (C99
+ * Annex F), which gives the alpha = 0 and alpha = 1 forms of [P2]. */
+void sqo_smooth_scales(const float *xa, const float *wa, int64_t K, float alpha, float *s)
+{
+    double a = (double)alpha;
+    for (int64_t j = 0; j < K; ++j) {
+        float x = xa[j] < SQO_EPS ? SQO_EPS : xa[j];
+        float w = wa[j] < SQO_EPS ? SQO_EPS : wa[j];
+        double num = pow((double)x, a);
+        double den = pow((double)w, 1.0 - a);
+        s[j] = (float)(num / den);
+    }
+}
+
+/* [P5] "The four operations": code = clamp(round(v / scale), -n, n), with
+ * round = nearest, ties to even (torch.round and np.round both do this). */
+static int8_t code_of(float v, float scale)
+{
+    float q = rintf(v / scale);               /* default mode: ties to even   */
+    if (q > (float)SQO_N) q = (float)SQO_N;   /* round first, then clamp      */
+    if (q < -(float)SQO_N) q = -(float)SQO_N;
+    return (int8_t)q;
+}
+
+/* Quantise one row of `len` smoothed values: scale = amax / 127; amax = 0 gives
+ * scale 1 and all codes 0 ([P5] zero-range case). */
+static void quantize_row(const float *v, int64_t len, int8_t *q, float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t k = 0; k < len; ++k) {
+        float a = fabsf(v[k]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale = 1.0f;
+        for (int64_t k = 0; k < len; ++k) q[k] = 0;
+        return;
+    }
+    float sc = amax / (float)SQO_N;
+    *scale = sc;
+    for (int64_t k = 0; k < len; ++k) q[k] = code_of(v[k], sc);
+}
+
+/* Offline weight preparation.  [P3]: multiply weight input-column j by s_j
+ * (W_hat = W diag(s)), then quantise per output channel (one scale per row n of
+ * W [N x K]).  s == NULL means no smoothing. */
+void sqo_quantize_weights(const float *W, int64_t N, int64_t K, const float *s,
+                          int8_t *Wq, float *w_scale)
+{
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k)
+                row[k] = s ? W[n * K + k] * s[k] : W[n * K + k];
+            quantize_row(row, K, Wq + n * K, w_scale + n);
+        }
+        free(row);
+    }
+}
+
+/* Dynamic per-token activation quantisation.  [P3]: divide activation channel j
+ * by s_j (X_hat = X diag(s)^-1); then one scale per token (row t of X [T x K]).
+ * s == NULL means the input is already smoothed. */
+void sqo_quant_act(const float *X, int64_t T, int64_t K, const float *s,
+                   int8_t *Xq, float *x_scale)
+{
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t k = 0; k < K; ++k)
+                row[k] = s ? X[t * K + k] / s[k] : X[t * K + k];
+            quantize_row(row, K, Xq + t * K, x_scale + t);
+        }
+        free(row);
+    }
+}
+
+/* Integer matmul.  [P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk.
+ * Accumulated in int64; returns 1 if any sum does not fit int32, else 0. */
+int sqo_int_gemm(const int8_t *Xq, const int8_t *Wq, int64_t T, int64_t N, int64_t K,
+                 int32_t *acc)
+{
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k)
+                sum += (int64_t)Xq[t * K + k] * (int64_t)Wq[n * K + k];
+            if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
+            acc[t * N + n] = (int32_t)sum;
+        }
+    return overflow;
+}
+
+/* The same sums for a list of (t, n) pairs only (for problems too large to
+ * multiply out on the CPU). */
+int sqo_int_gemm_at(const int8_t *Xq, const int8_t *Wq, int64_t K, const int64_t *ti,
+                    const int64_t *ni, int64_t count, int32_t *acc)
+{
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t sum = 0;
+        for (int64_t k = 0; k < K; ++k)
+            sum += (int64_t)Xq[ti[i] * K + k] * (int64_t)Wq[ni[i] * K + k];
+        if (sum > INT32_MAX || sum < INT32_MIN) overflow = 1;
+        acc[i] = (int32_t)sum;
+    }
+    return overflow;
+}
+
+/* Dequantising epilogue.  [P4] "integer matmul, float epilogue": the integer
+ * result times (sx * sw); [P3] per-token and per-output-channel scales applied
+ * in the epilogue.  y = fl32( fl32(acc) * fl32(x_scale[t] * w_scale[n]) ). */
+void sqo_dequant(const int32_t *acc, const float *x_scale, const float *w_scale,
+                 int64_t T, int64_t N, float *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            float sxw = x_scale[t] * w_scale[n];
+            y[t * N + n] = (float)acc[t * N + n] * sxw;
+        }
+}
+
+/* Same epilogue for a list of pairs (acc[i] belongs to (ti[i], ni[i])). */
+void sqo_dequant_at(const int32_t *acc, const float *x_scale, const float *w_scale,
+                    const int64_t *ti, const int64_t *ni, int64_t count, float *y)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        float sxw = x_scale[ti[i]] * w_scale[ni[i]];
+        y[i] = (float)acc[i] * sxw;
+    }
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even (finite inputs). */
+void sqo_to_bf16(const float *y, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &y[i], sizeof u);
+        uint32_t lower = u & 0xFFFFu;
+        uint32_t upper = u >> 16;
+        if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+        out[i] = (uint16_t)upper;
+    }
+}

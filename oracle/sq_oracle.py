@@ -1,0 +1,247 @@
+"""NumPy front end of the plain C oracle (sq_oracle.c) -- TEST INFRASTRUCTURE.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg use this module;
+the product path must never import it.  It shares no code with the HIP library.
+
+Each function cites the passage it follows (pages by title, section named):
+  [P2] multigrid.ai "SmoothQuant Explained"
+  [P3] inferenceinterviews.com "Why do activation outliers break INT8 W8A8..."
+  [P4] mercemay.com "Activation Outlier Channels and Mixed-Precision Decomposition"
+  [P5] maitreyasuin.github.io "...01-one-outlier"
+
+bf16 inputs are widened to float32 exactly before they reach the C code; the
+diagnostics (exact product, relative error, channel ratios) are float64.
+
+Parity pins of every function live in tests/test_oracle_pins.py; none of the
+functions here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsqoracle.so")
+_lib = None
+_lock = threading.Lock()
+
+__all__ = ["build", "col_absmax", "smooth_scales", "quantize_weights", "quant_act",
+           "int_gemm", "int_gemm_at", "dequant", "dequant_at", "to_bf16", "w8a8_linear",
+           "prepare", "w8a8_relative_error", "channel_max_over_median", "exact_product",
+           "widen_bf16", "set_threads"]
+
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+             "-std=c11", "-Wall"]
+
+
+def build(force: bool = False) -> str:
+    """Compile sq_oracle.c with gcc into oracle/libsqoracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            F = ctypes.c_float
+            lib.sqo_col_absmax.argtypes = [P, I64, I64, P]
+            lib.sqo_smooth_scales.argtypes = [P, P, I64, F, P]
+            lib.sqo_quantize_weights.argtypes = [P, I64, I64, P, P, P]
+            lib.sqo_quant_act.argtypes = [P, I64, I64, P, P, P]
+            lib.sqo_int_gemm.argtypes = [P, P, I64, I64, I64, P]
+            lib.sqo_int_gemm.restype = ctypes.c_int
+            lib.sqo_int_gemm_at.argtypes = [P, P, I64, P, P, I64, P]
+            lib.sqo_int_gemm_at.restype = ctypes.c_int
+            lib.sqo_dequant.argtypes = [P, P, P, I64, I64, P]
+            lib.sqo_dequant_at.argtypes = [P, P, P, P, P, I64, P]
+            lib.sqo_to_bf16.argtypes = [P, I64, P]
+            for f in ("sqo_col_absmax", "sqo_smooth_scales", "sqo_quantize_weights",
+                      "sqo_quant_act", "sqo_dequant", "sqo_dequant_at", "sqo_to_bf16"):
+                getattr(lib, f).restype = None
+            _lib = lib
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    """OpenMP thread count for the oracle (the CPU baseline reports it)."""
+    os.environ["OMP_NUM_THREADS"] = str(n)
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(ctypes.c_int(n))
+    except OSError:
+        pass
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """uint16 bf16 patterns -> float32, exactly (the bits become the high half)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def col_absmax(A: np.ndarray) -> np.ndarray:
+    """[P3] max_t |X_tj| (activations) or max_n |W_nj| (weights), per column j."""
+    A = _f32(A)
+    out = np.empty(A.shape[1], np.float32)
+    _load().sqo_col_absmax(_ptr(A), A.shape[0], A.shape[1], _ptr(out))
+    return out
+
+
+def smooth_scales(x_absmax, w_absmax, alpha: float) -> np.ndarray:
+    """[P2] section "Alpha: how much difficulty to move"; [P3] "A strong answer";
+    [P5] "Route it, or move it" (maxima clamped at 1e-8):
+    s_j = max(xa_j, 1e-8)^alpha / max(wa_j, 1e-8)^(1 - alpha), binary64 then
+    rounded to binary32."""
+    xa, wa = _f32(x_absmax), _f32(w_absmax)
+    assert xa.shape == wa.shape
+    s = np.empty_like(xa)
+    _load().sqo_smooth_scales(_ptr(xa), _ptr(wa), xa.size, float(alpha), _ptr(s))
+    return s
+
+
+def quantize_weights(W, s=None):
+    """[P3] W_hat = W diag(s); per-output-channel symmetric int8 ([P5] "The four
+    operations").  Returns (Wq int8 [N,K], w_scale float32 [N])."""
+    W = _f32(W)
+    N, K = W.shape
+    s = None if s is None else _f32(s)
+    Wq = np.empty((N, K), np.int8)
+    ws = np.empty(N, np.float32)
+    _load().sqo_quantize_weights(_ptr(W), N, K, _ptr(s), _ptr(Wq), _ptr(ws))
+    return Wq, ws
+
+
+def quant_act(X, s=None):
+    """[P3] X_hat = X diag(s)^-1; dynamic per-token symmetric int8 ([P5] "The
+    four operations").  Returns (Xq int8 [T,K], x_scale float32 [T])."""
+    X = _f32(X)
+    T, K = X.shape
+    s = None if s is None else _f32(s)
+    Xq = np.empty((T, K), np.int8)
+    xs = np.empty(T, np.float32)
+    _load().sqo_quant_act(_ptr(X), T, K, _ptr(s), _ptr(Xq), _ptr(xs))
+    return Xq, xs
+
+
+def int_gemm(Xq, Wq):
+    """[P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk, exact int32."""
+    Xq = np.ascontiguousarray(Xq, np.int8)
+    Wq = np.ascontiguousarray(Wq, np.int8)
+    T, K = Xq.shape
+    N, K2 = Wq.shape
+    assert K == K2
+    acc = np.empty((T, N), np.int32)
+    if _load().sqo_int_gemm(_ptr(Xq), _ptr(Wq), T, N, K, _ptr(acc)):
+        raise OverflowError("integer accumulator does not fit int32")
+    return acc
+
+
+def int_gemm_at(Xq, Wq, ti, ni):
+    """acc at the listed (t, n) pairs only."""
+    Xq = np.ascontiguousarray(Xq, np.int8)
+    Wq = np.ascontiguousarray(Wq, np.int8)
+    ti = np.ascontiguousarray(ti, np.int64)
+    ni = np.ascontiguousarray(ni, np.int64)
+    assert ti.shape == ni.shape and Xq.shape[1] == Wq.shape[1]
+    assert ti.size == 0 or (ti.min() >= 0 and ti.max() < Xq.shape[0])
+    assert ni.size == 0 or (ni.min() >= 0 and ni.max() < Wq.shape[0])
+    acc = np.empty(ti.size, np.int32)
+    if _load().sqo_int_gemm_at(_ptr(Xq), _ptr(Wq), Xq.shape[1], _ptr(ti), _ptr(ni),
+                               ti.size, _ptr(acc)):
+        raise OverflowError("integer accumulator does not fit int32")
+    return acc
+
+
+def dequant(acc, x_scale, w_scale):
+    """[P4] section "Decomposition": (qx @ qW.T) * (sx * sw) --
+    y = fl32(fl32(acc) * fl32(xs_t * ws_n))."""
+    acc = np.ascontiguousarray(acc, np.int32)
+    xs, ws = _f32(x_scale), _f32(w_scale)
+    T, N = acc.shape
+    assert xs.size == T and ws.size == N
+    y = np.empty((T, N), np.float32)
+    _load().sqo_dequant(_ptr(acc), _ptr(xs), _ptr(ws), T, N, _ptr(y))
+    return y
+
+
+def dequant_at(acc, x_scale, w_scale, ti, ni):
+    acc = np.ascontiguousarray(acc, np.int32)
+    xs, ws = _f32(x_scale), _f32(w_scale)
+    ti = np.ascontiguousarray(ti, np.int64)
+    ni = np.ascontiguousarray(ni, np.int64)
+    y = np.empty(acc.size, np.float32)
+    _load().sqo_dequant_at(_ptr(acc), _ptr(xs), _ptr(ws), _ptr(ti), _ptr(ni), acc.size, _ptr(y))
+    return y
+
+
+def to_bf16(y) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), nearest, ties to even."""
+    y = _f32(y)
+    out = np.empty(y.shape, np.uint16)
+    _load().sqo_to_bf16(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def prepare(X_stats, W, alpha):
+    """Offline half of the layer: statistics, smoothing factors, smoothed and
+    quantised weights.  alpha=None means no smoothing (s is None)."""
+    if alpha is None:
+        Wq, ws = quantize_weights(W, None)
+        return dict(s=None, x_absmax=None, w_absmax=None, Wq=Wq, w_scale=ws)
+    xa = col_absmax(X_stats)
+    wa = col_absmax(W)
+    s = smooth_scales(xa, wa, alpha)
+    Wq, ws = quantize_weights(W, s)
+    return dict(s=s, x_absmax=xa, w_absmax=wa, Wq=Wq, w_scale=ws)
+
+
+def w8a8_linear(X, s, Wq, w_scale):
+    """Runtime half: per-token quantisation of X diag(s)^-1, integer GEMM,
+    epilogue.  Returns (y float32 [T,N], Xq, x_scale, acc)."""
+    Xq, xs = quant_act(X, s)
+    acc = int_gemm(Xq, Wq)
+    return dequant(acc, xs, w_scale), Xq, xs, acc
+
+
+def exact_product(X, W):
+    """Y = X W^T in float64 ([P5]: Y = X W^T, X in R^{T x K}, W in R^{N x K})."""
+    return np.asarray(X, np.float64) @ np.asarray(W, np.float64).T
+
+
+def w8a8_relative_error(X, W, alpha):
+    """[P3] relative Frobenius error ||Y_q - Y|| / ||Y|| of the W8A8 layer with
+    per-token activations and per-output-channel weights; alpha=None: no
+    smoothing.  Statistics are taken from X itself, as in [P3]'s experiment."""
+    X32, W32 = _f32(X), _f32(W)
+    p = prepare(X32, W32, alpha)
+    y, *_ = w8a8_linear(X32, p["s"], p["Wq"], p["w_scale"])
+    Y = exact_product(X, W)
+    return float(np.linalg.norm(y.astype(np.float64) - Y) / np.linalg.norm(Y))
+
+
+def channel_max_over_median(A):
+    """[P3] table "alpha / act max/median / weight max/median": the largest
+    per-input-channel max divided by the median per-input-channel max (median of
+    an even count is the mean of the two middle values)."""
+    m = col_absmax(A).astype(np.float64)
+    return float(m.max() / np.median(m))

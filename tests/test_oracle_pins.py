@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+printed value on a page (tests/golden/*), a closed form, an invariant, a textbook
+or library routine, or brute force on tiny inputs.  A plausible slip in the oracle
+(wrong axis, multiply instead of divide, dropped clamp, truncation instead of
+round-half-even, swapped scale) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------- page 3 numbers
+@pytest.fixture(scope="module")
+def page3():
+    X, W, cols = WL.page3_experiment_data()
+    return X, W, cols
+
+
+def _golden_page3():
+    g = {}
+    sweep = []
+    for row in read_golden("page3_experiment.txt"):
+        if row[0] == "sweep":
+            sweep.append(tuple(float(v) for v in row[1:]))
+        else:
+            g[row[0]] = float(row[1])
+    return g, sweep
+
+
+def test_page3_error_before_after(page3):
+    """inferenceinterviews.com page, "A strong answer": before 0.0949 after 0.0181."""
+    X, W, _ = page3
+    g, _ = _golden_page3()
+    assert round(O.w8a8_relative_error(X, W, None), 4) == g["error_before"]
+    assert round(O.w8a8_relative_error(X, W, 0.5), 4) == g["error_after_alpha_0.5"]
+
+
+def test_page3_outlier_severity(page3):
+    """Same page: largest channel max / median channel max = 73; 127/73 = 1.7."""
+    X, _, _ = page3
+    g, _ = _golden_page3()
+    r = O.channel_max_over_median(X.astype(np.float32))
+    assert round(r) == g["act_ratio_before"]
+    assert round(127 / round(r), 1) == g["steps_left"]
+
+
+def test_page3_alpha_sweep(page3):
+    """Same page, alpha table: act and weight max/median and W8A8 error per alpha."""
+    X, W, _ = page3
+    _, sweep = _golden_page3()
+    X32, W32 = X.astype(np.float32), W.astype(np.float32)
+    xa, wa = O.col_absmax(X32), O.col_absmax(W32)
+    for alpha, act_r, w_r, err_pct in sweep:
+        s = O.smooth_scales(xa, wa, alpha)
+        Xh = X32 / s          # smoothed activations (fp32, as the layer sees them)
+        Wh = W32 * s
+        assert round(O.channel_max_over_median(Xh), 1) == act_r, alpha
+        assert round(O.channel_max_over_median(Wh), 1) == w_r, alpha
+        assert round(100 * O.w8a8_relative_error(X, W, alpha), 1) == err_pct, alpha
+
+
+def test_page3_qualitative_drop_only_inside(page3):
+    """Smoothing helps at alpha in [0.25, 0.75] on the page data; the endpoints
+    are not asserted to help (alpha = 1 is worse than no smoothing, as printed)."""
+    X, W, _ = page3
+    before = O.w8a8_relative_error(X, W, None)
+    for a in (0.25, 0.5, 0.75):
+        assert O.w8a8_relative_error(X, W, a) < before
+    assert O.w8a8_relative_error(X, W, 1.0) > before
+
+
+# ------------------------------------------------------------ worked example (P4)
+def test_worked_example_p4():
+    """mercemay.com page, "Why the per-tensor scale cannot fix it": amax 30 gives
+    scale about 0.236; 0.01 -> code 0; 0.5 -> code 2."""
+    rows = {r[0]: r[1:] for r in read_golden("worked_example_p4.txt") if r[0] != "code"}
+    codes = [r[1:] for r in read_golden("worked_example_p4.txt") if r[0] == "code"]
+    L = int(rows["length"][0])
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-0.99, 0.99, size=L).astype(np.float32)
+    x[17] = float(rows["amax"][0])
+    probe = {}
+    for i, (v, _) in enumerate(codes):
+        x[100 + i] = float(v)
+        probe[100 + i] = codes[i]
+    Xq, xs = O.quant_act(x[None, :], None)
+    assert round(float(xs[0]), int(rows["scale_decimals"][0])) == float(rows["scale_approx"][0])
+    for i, (v, c) in probe.items():
+        assert int(Xq[0, i]) == int(c), v
+    assert Xq[0, 17] == 127
+
+
+# ------------------------------------------------------------ quantizer (P5 rules)
+def test_zero_rows_give_scale_one_and_zero_codes():
+    """maitreyasuin page, "The four operations": an all-zero tensor gives codes 0
+    and scale 1.0 (no 0/0)."""
+    rules = {r[0]: r[1] for r in read_golden("quantizer_rules_p5.txt")}
+    X = np.zeros((3, 40), np.float32)
+    X[1, 5] = 2.0
+    Xq, xs = O.quant_act(X, None)
+    assert xs[0] == float(rules["zero_scale"]) and xs[2] == float(rules["zero_scale"])
+    assert not Xq[0].any() and not Xq[2].any()
+    Wq, ws = O.quantize_weights(X, None)
+    assert ws[0] == 1.0 and not Wq[0].any()
+    # with smoothing, a zero row stays zero
+    s = np.linspace(0.5, 3, 40).astype(np.float32)
+    Xq, xs = O.quant_act(X, s)
+    assert xs[0] == 1.0 and not Xq[0].any()
+
+
+def test_round_half_even_ties():
+    """Ties go to even (np.round / torch.round semantics used on the pages).  A row
+    with amax 127 has scale exactly 1, so x/scale is x itself."""
+    vals = [127.0, 0.5, 1.5, 2.5, -2.5, -0.5, 3.5, 126.5, -126.5, 0.49999997, 2.5000002]
+    want = [127, 0, 2, 2, -2, 0, 4, 126, -126, 0, 3]
+    X = np.array([vals], np.float32)
+    Xq, xs = O.quant_act(X, None)
+    assert xs[0] == 1.0
+    assert Xq[0].tolist() == want
+    Wq, ws = O.quantize_weights(X, None)
+    assert ws[0] == 1.0 and Wq[0].tolist() == want
+
+
+def test_code_range_and_full_scale():
+    """Codes stay in [-127, 127] (never -128), and every nonzero row reaches
+    |code| = 127 exactly at its absmax element."""
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((64, 300)) * rng.uniform(0.01, 100, (64, 1))).astype(np.float32)
+    X[3] = -X[3]
+    s = rng.uniform(0.1, 10, 300).astype(np.float32)
+    for Xq, _ in (O.quant_act(X, s), O.quantize_weights(X, s)):
+        assert Xq.min() >= -127 and Xq.max() <= 127
+        assert (np.abs(Xq.astype(np.int32)).max(axis=1) == 127).all()
+    Xq, _ = O.quant_act(X, s)
+    am = np.argmax(np.abs(X / s), axis=1)
+    assert (np.abs(Xq[np.arange(64), am]) == 127).all()
+
+
+def test_round_trip_error_within_half_step():
+    """x_hat = s q ("The four operations") is within half a step of x for every
+    element, and the sign is kept: pins division by the scale (not
+    multiplication) and nearest rounding (not truncation)."""
+    rng = np.random.default_rng(12)
+    X = (rng.standard_normal((50, 257)) * 3).astype(np.float32)
+    s = rng.uniform(0.2, 5, 257).astype(np.float32)
+    Xq, xs = O.quant_act(X, s)
+    Xh = X.astype(np.float64) / s.astype(np.float64)
+    deq = Xq.astype(np.float64) * xs[:, None].astype(np.float64)
+    step = xs[:, None].astype(np.float64)
+    assert (np.abs(deq - Xh) <= 0.5 * step * (1 + 1e-5)).all()
+    assert (np.sign(Xq) * np.sign(Xh) >= 0).all()
+    # nearest rounding leaves a quarter step on average; truncation half a step
+    assert np.mean(np.abs(deq - Xh) / step) < 0.3
+    # weights: the smoothing factor multiplies (W diag(s))
+    Wq, ws = O.quantize_weights(X, s)
+    Wh = X.astype(np.float64) * s.astype(np.float64)
+    deqw = Wq.astype(np.float64) * ws[:, None].astype(np.float64)
+    assert (np.abs(deqw - Wh) <= 0.5 * ws[:, None] * (1 + 1e-5)).all()
+
+
+def test_scale_is_amax_over_127():
+    """scale = limit / n with n = 127 ("The four operations")."""
+    X = np.array([[0.0, -30.0, 3.0, 1.0], [254.0, 1.0, 2.0, -1.0]], np.float32)
+    _, xs = O.quant_act(X, None)
+    assert xs[0] == np.float32(30.0) / np.float32(127.0)
+    assert xs[1] == np.float32(2.0)
+
+
+# ----------------------------------------------------------- smoothing factors
+def test_alpha_closed_forms():
+    """multigrid.ai page, "Alpha: how much difficulty to move": alpha = 0 gives
+    s = 1 / max|W_j|; alpha = 1 gives s = max|X_j|."""
+    rng = np.random.default_rng(3)
+    xa = rng.uniform(0.01, 200, 999).astype(np.float32)
+    wa = rng.uniform(1e-3, 2, 999).astype(np.float32)
+    s0 = O.smooth_scales(xa, wa, 0.0)
+    s1 = O.smooth_scales(xa, wa, 1.0)
+    assert np.array_equal(s1, xa)
+    assert np.array_equal(s0, (np.float32(1.0) / wa).astype(np.float32))
+
+
+def test_alpha_half_balances_maxima():
+    """alpha = 0.5 is the geometric balance: after smoothing, each channel's
+    activation max equals its weight max (maitreyasuin page, "Route it, or move
+    it": both maxima become 3.86); for any alpha the product of the two maxima is
+    unchanged, and s_j is monotone in alpha towards the activation side."""
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((200, 64)).astype(np.float32)
+    X[:, [3, 40]] *= 50
+    W = (rng.standard_normal((90, 64)) * 0.02).astype(np.float32)
+    xa, wa = O.col_absmax(X), O.col_absmax(W)
+    s = O.smooth_scales(xa, wa, 0.5)
+    xh = np.abs(X / s).max(0)
+    wh = np.abs(W * s).max(0)
+    np.testing.assert_allclose(xh, wh, rtol=1e-6)
+    for a in (0.0, 0.3, 0.75, 1.0):
+        s = O.smooth_scales(xa, wa, a)
+        np.testing.assert_allclose(np.abs(X / s).max(0) * np.abs(W * s).max(0),
+                                   xa.astype(np.float64) * wa, rtol=1e-6)
+    ratio = xa.astype(np.float64) * wa
+    s_lo, s_hi = O.smooth_scales(xa, wa, 0.25), O.smooth_scales(xa, wa, 0.75)
+    # d log s / d alpha = log(xa * wa): s grows with alpha exactly where xa*wa > 1
+    clear = np.abs(np.log(ratio)) > 1e-3
+    assert np.array_equal((s_hi > s_lo)[clear], (ratio > 1)[clear])
+
+
+def test_smoothing_eps_clamp():
+    """maitreyasuin page, "Route it, or move it": both maxima clamped below at
+    1e-8 before the powers, so zero columns give finite factors."""
+    xa = np.array([0.0, 0.0, 2.0], np.float32)
+    wa = np.array([0.0, 4.0, 0.0], np.float32)
+    eps = np.float32(1e-8)
+    assert np.array_equal(O.smooth_scales(xa, wa, 1.0), np.array([eps, eps, 2.0], np.float32))
+    s0 = O.smooth_scales(xa, wa, 0.0)
+    assert s0[0] == np.float32(1.0 / np.float64(eps)) and s0[1] == np.float32(0.25)
+    assert np.isfinite(O.smooth_scales(xa, wa, 0.5)).all()
+
+
+def test_col_absmax_brute_force():
+    """Column absmax against a plain loop and numpy's reduction."""
+    rng = np.random.default_rng(9)
+    A = rng.standard_normal((13, 7)).astype(np.float32)
+    A[4, 2] = -99.0
+    got = O.col_absmax(A)
+    want = [max(abs(float(A[i, j])) for i in range(13)) for j in range(7)]
+    assert got.tolist() == want
+    assert np.array_equal(got, np.abs(A).max(axis=0))
+
+
+def test_smoothing_identity_fp64():
+    """XW^T = (X diag(s)^-1)(W diag(s))^T exactly over the reals (inferenceinterviews
+    page, "What SmoothQuant does"; maitreyasuin page, "Route it, or move it"); in
+    fp64 the relative difference is at rounding level (<= 1e-12), with the
+    oracle's factors applied on the column (input-channel) axis."""
+    w = WL.make("tiny_t128_k1024_n1024")
+    xa, wa = O.col_absmax(w.X), O.col_absmax(w.W)
+    s = O.smooth_scales(xa, wa, 0.5).astype(np.float64)
+    X, W = w.X.astype(np.float64), w.W.astype(np.float64)
+    Y = X @ W.T
+    Ys = (X / s) @ (W * s).T
+    assert np.linalg.norm(Ys - Y) / np.linalg.norm(Y) <= 1e-12
+    # a factor applied on the wrong axis does not cancel
+    bad = (X / s) @ W.T
+    assert np.linalg.norm(bad - Y) / np.linalg.norm(Y) > 1e-2
+
+
+def test_quantized_pipeline_tracks_smoothed_operands():
+    """With the oracle's own quantizers, the dequantised smoothed operands
+    multiply back to XW^T (orientation of s on both sides is right)."""
+    w = WL.make("tiny_t128_k1024_n1024")
+    p = O.prepare(w.X, w.W, 0.5)
+    y, Xq, xs, acc = O.w8a8_linear(w.X, p["s"], p["Wq"], p["w_scale"])
+    Y = O.exact_product(w.X, w.W)
+    assert np.linalg.norm(y - Y) / np.linalg.norm(Y) < 0.03
+
+
+# -------------------------------------------------------------- integer GEMM
+@pytest.mark.parametrize("T,N,K", [(1, 1, 1), (3, 17, 64), (17, 3, 17), (64, 5, 3), (4, 64, 1)])
+def test_int_gemm_brute_force(T, N, K):
+    """acc_tn = sum_k P_tk Q_nk: pure-Python triple loop and an fp64 BLAS product
+    (exact while |acc| < 2^53) agree with the oracle."""
+    rng = np.random.default_rng(T * 1000 + N * 10 + K)
+    Xq = rng.integers(-127, 128, (T, K), dtype=np.int8)
+    Wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    acc = O.int_gemm(Xq, Wq)
+    for t in range(T):
+        for n in range(N):
+            assert acc[t, n] == sum(int(Xq[t, k]) * int(Wq[n, k]) for k in range(K))
+    assert np.array_equal(acc, (Xq.astype(np.float64) @ Wq.astype(np.float64).T).astype(np.int64))
+    ti = rng.integers(0, T, 9)
+    ni = rng.integers(0, N, 9)
+    assert np.array_equal(O.int_gemm_at(Xq, Wq, ti, ni), acc[ti, ni])
+
+
+def test_int_gemm_extremes_and_overflow():
+    """|acc| <= 127^2 K fits int32 up to K = 133144; one more overflows."""
+    K = 133144
+    Xq = np.full((1, K), 127, np.int8)
+    Wq = np.full((2, K), 127, np.int8)
+    Wq[1] = -127
+    acc = O.int_gemm(Xq, Wq)
+    assert acc[0, 0] == 127 * 127 * K and acc[0, 1] == -127 * 127 * K
+    Xq2 = np.full((1, K + 1), 127, np.int8)
+    with pytest.raises(OverflowError):
+        O.int_gemm(Xq2, np.full((1, K + 1), 127, np.int8))
+
+
+# ------------------------------------------------------------------ epilogue
+def test_epilogue_factors_out():
+    """maitreyasuin page, "Which scales factor out, and why": per-token and
+    per-output-channel scales come out of the sum, so acc * (a_t * s_n) equals the
+    fp64 product of the dequantised operands up to the two fp32 roundings of the
+    epilogue (<= 2^-23 relative)."""
+    rng = np.random.default_rng(21)
+    Xq = rng.integers(-127, 128, (31, 70), dtype=np.int8)
+    Wq = rng.integers(-127, 128, (23, 70), dtype=np.int8)
+    xs = rng.uniform(0.001, 2, 31).astype(np.float32)
+    ws = rng.uniform(0.0001, 0.1, 23).astype(np.float32)
+    y = O.dequant(O.int_gemm(Xq, Wq), xs, ws).astype(np.float64)
+    ref = (Xq * xs[:, None].astype(np.float64)) @ (Wq * ws[:, None].astype(np.float64)).T
+    np.testing.assert_allclose(y, ref, rtol=2 ** -22, atol=0)
+    # swapping the two scale vectors' roles breaks it
+    bad = O.dequant(O.int_gemm(Xq, Wq)[:23, :23], ws, xs[:23]).astype(np.float64)
+    assert not np.allclose(bad, ref[:23, :23], rtol=1e-3)
+    yat = O.dequant_at(O.int_gemm(Xq, Wq)[[0, 5], [1, 7]], xs, ws, [0, 5], [1, 7])
+    assert np.array_equal(yat, y[[0, 5], [1, 7]].astype(np.float32))
+
+
+def test_epilogue_order_is_product_of_scales_first():
+    """The epilogue multiplies by (sx * sw) formed first ("integer matmul, float
+    epilogue" on the mercemay page); for a case where the two orders round apart
+    the oracle takes this one."""
+    rng = np.random.default_rng(8)
+    acc = rng.integers(-2 ** 24, 2 ** 24, (1, 4000)).astype(np.int32)
+    xs = np.array([0.1], np.float32)
+    ws = rng.uniform(1e-3, 1, 4000).astype(np.float32)
+    y = O.dequant(acc, xs, ws)[0]
+    first = acc[0].astype(np.float32) * (xs[0] * ws)
+    assert np.array_equal(y, first.astype(np.float32))
+    other = (acc[0].astype(np.float32) * xs[0]) * ws
+    assert not np.array_equal(y, other)
+
+
+def test_bf16_rounding():
+    """float32 -> bf16 nearest-even against torch's conversion, plus hand cases."""
+    import torch
+    rng = np.random.default_rng(2)
+    y = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    hand = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20, 0.0, -0.0],
+                    np.float32)
+    want = [0x3F80, 0x3F80, 0x3F82, 0xBF80, 0x3F81, 0x0000, 0x8000]
+    assert O.to_bf16(hand).tolist() == want
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.to_bf16(y), ref)
+
+
+# -------------------------------------------------------- qualitative drop
+@pytest.mark.parametrize("name,tokens,alpha", [("tiny_t128_k1024_n1024", None, 0.5),
+                                               ("page_t512_k4096_n4096", 128, 0.5)])
+def test_smoothing_lowers_error_on_outlier_data(name, tokens, alpha):
+    """W8A8 error after smoothing is below the error without it on outlier data
+    (inferenceinterviews page: 9.5% -> 1.8%)."""
+    w = WL.make(name, tokens=tokens)
+    W = w.W if tokens is None else w.W[:1024]
+    before = O.w8a8_relative_error(w.X, W, None)
+    after = O.w8a8_relative_error(w.X, W, alpha)
+    assert after < 0.5 * before
+
+
+def test_smoothing_lowers_error_heavy_outliers():
+    """Heavy-outlier structure (30% of channels x10..x60, alpha 0.75) at a reduced
+    size: smoothing still lowers the error."""
+    w = WL.make_linear(256, 512, 2048, n_out=614, mult_range=(10., 60.), seed=99)
+    before = O.w8a8_relative_error(w.X, w.W, None)
+    after = O.w8a8_relative_error(w.X, w.W, 0.75)
+    assert after < before
+
+
+def test_oracle_threads_independent():
+    """Results do not depend on the OpenMP thread count (max and integer sums are
+    order-free; each row is independent)."""
+    w = WL.page_tiny_fixture()
+    p = O.prepare(w.X, w.W, 0.5)
+    y1 = O.w8a8_linear(w.X, p["s"], p["Wq"], p["w_scale"])[0]
+    O.set_threads(1)
+    try:
+        y2 = O.w8a8_linear(w.X, p["s"], p["Wq"], p["w_scale"])[0]
+    finally:
+        O.set_threads(8)
+    assert np.array_equal(y1, y2)
+    assert math.isfinite(float(np.abs(y1).max()))
