@@ -1,0 +1,187 @@
+/*
+ * sq.h -- C ABI of the SmoothQuant W8A8 linear layer on MI355X (gfx950).
+ *
+ * The layer computes Y = X W^T with X [T x K] activations (T tokens, K input
+ * channels) and W [N x K] weights (N output channels), rewritten exactly as
+ *     Y = (X diag(s)^-1) (W diag(s))^T
+ * (inferenceinterviews.com, "Why do activation outliers break INT8 W8A8 on
+ * LLMs...", section "A strong answer"; maitreyasuin.github.io "...01-one-outlier",
+ * section "Route it, or move it"), then quantises both smoothed operands to
+ * symmetric int8 and multiplies them in integer arithmetic:
+ *   - offline: per-input-channel smoothing factors s from column absolute maxima,
+ *     W diag(s) quantised with one scale per output channel;
+ *   - at run time: X diag(s)^-1 quantised with one scale per token, computed
+ *     from the values present (dynamic), then an int8 x int8 -> int32 GEMM whose
+ *     epilogue multiplies by the token scale times the channel scale.
+ *
+ * Quantiser (maitreyasuin page, section "The four operations"): for one row v,
+ * amax = max |v|; scale = amax / 127 (binary32 division); code =
+ * clamp(round_half_even(v / scale), -127, 127).  -128 is never produced.  A row
+ * with amax = 0 gets scale 1.0 and all codes 0.
+ *
+ * Conventions common to every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never frees or retains them.  Matrices are row-major and contiguous: X and
+ *     Xq are [T][K], W and Wq are [N][K] (K contiguous), Y is [T][N].
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; no call synchronises the stream or allocates device
+ *     memory.  Outputs are valid once the stream reaches the enqueued work.
+ *   - Arguments are validated on the host before anything is enqueued.  On any
+ *     error other than SQ_ERR_HIP nothing is launched and no output is written.
+ *     SQ_ERR_HIP means a kernel launch was rejected by the HIP runtime; outputs
+ *     are then unspecified.
+ *   - Calls are thread-safe.  The only library state is a per-device cache of
+ *     device attributes.
+ *   - NaN and infinite inputs are outside the contract.
+ *   - Any T, N, K >= 1 is accepted.  Rows whose byte length is a multiple of 16
+ *     with 16-byte aligned base pointers take the vectorised kernels; other
+ *     shapes take slower scalar kernels with identical results.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sq_status {
+    SQ_OK = 0,
+    SQ_ERR_NULL = 1,       /* a required pointer is NULL                         */
+    SQ_ERR_SHAPE = 2,      /* a size is < 1, or K exceeds SQ_MAX_K for the GEMM  */
+    SQ_ERR_ALPHA = 3,      /* alpha is NaN or outside [0, 1]                     */
+    SQ_ERR_DTYPE = 4,      /* dtype not accepted for that argument               */
+    SQ_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required            */
+    SQ_ERR_HIP = 6         /* the HIP runtime rejected a launch                  */
+} sq_status;
+
+typedef enum sq_dtype {
+    SQ_F32 = 0,            /* IEEE binary32                                      */
+    SQ_BF16 = 1,           /* bfloat16 (upper half of a binary32)                */
+    SQ_I32 = 2             /* int32; only as GEMM output: the raw accumulators   */
+} sq_dtype;
+
+/* Largest K for which 127 * 127 * K fits in int32, so the GEMM's int32
+ * accumulators cannot overflow. */
+#define SQ_MAX_K 133144
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *sq_status_string(sq_status status);
+
+/*
+ * Column absolute maximum of a [rows x cols] matrix:
+ *     amax[j] = max_i |A[i][j]|            (or max(amax[j], that) if accumulate)
+ * These are the statistics max_t |X_tj| and max_n |W_nj| of the smoothing factor
+ * (inferenceinterviews page, "A strong answer"; maitreyasuin page, "Route it, or
+ * move it").  accumulate = 1 keeps a running maximum across calls (calibration
+ * over several batches); amax must then hold non-negative values already.
+ *   A     device, a_t = SQ_F32 or SQ_BF16, [rows][cols]
+ *   amax  device float [cols], written (read too if accumulate)
+ */
+sq_status sq_col_absmax(const void *A, sq_dtype a_t, int64_t rows, int64_t cols,
+                        float *amax, int accumulate, hipStream_t stream);
+
+/*
+ * Smoothing factors from precomputed column maxima (multigrid.ai "SmoothQuant
+ * Explained", section "Alpha: how much difficulty to move"; maxima clamped below
+ * at 1e-8 as on the maitreyasuin page, "Route it, or move it"):
+ *     s[j] = max(xa[j], 1e-8)^alpha / max(wa[j], 1e-8)^(1 - alpha)
+ * evaluated in binary64 and rounded once to binary32; alpha = 0 gives exactly
+ * 1 / max(wa, 1e-8) and alpha = 1 exactly max(xa, 1e-8).
+ *   x_absmax, w_absmax  device float [K];   s  device float [K], written
+ */
+sq_status sq_smooth_scales_from_absmax(const float *x_absmax, const float *w_absmax,
+                                       int64_t K, float alpha, float *s,
+                                       hipStream_t stream);
+
+/*
+ * Smoothing factors from a calibration batch X [T x K] and the weights W [N x K]:
+ * the two column maxima above followed by the formula above.  The maxima are
+ * returned too.
+ *   X         device, x_t = SQ_F32 or SQ_BF16, [T][K]
+ *   W         device, w_t = SQ_F32 or SQ_BF16, [N][K]
+ *   s         device float [K], written
+ *   x_absmax  device float [K], written (max_t |X_tj|)
+ *   w_absmax  device float [K], written (max_n |W_nj|)
+ */
+sq_status sq_smooth_scales(const void *X, sq_dtype x_t, int64_t T,
+                           const void *W, sq_dtype w_t, int64_t N, int64_t K,
+                           float alpha, float *s, float *x_absmax, float *w_absmax,
+                           hipStream_t stream);
+
+/*
+ * Offline weight preparation: W_hat = W diag(s) (binary32 multiply), then one
+ * symmetric int8 scale per output channel n (row of W):
+ *     w_scale[n] = max_k |W_hat[n][k]| / 127,  Wq[n][k] = code of W_hat[n][k]
+ * (inferenceinterviews page, "A strong answer": the weight input-columns absorb
+ * s before quantisation; per-output-channel scales factor out of the sum,
+ * maitreyasuin page, "Which scales factor out, and why").
+ *   W        device, w_t = SQ_F32 or SQ_BF16, [N][K]
+ *   s        device float [K], or NULL for no smoothing
+ *   Wq       device int8 [N][K], written;  w_scale  device float [N], written
+ */
+sq_status sq_quantize_weights(const void *W, sq_dtype w_t, int64_t N, int64_t K,
+                              const float *s, int8_t *Wq, float *w_scale,
+                              hipStream_t stream);
+
+/*
+ * Dynamic per-token activation quantisation fused with the smoothing division:
+ *     X_hat[t][k] = X[t][k] / s[k]          (binary32, correctly rounded)
+ *     x_scale[t]  = max_k |X_hat[t][k]| / 127,  Xq[t][k] = code of X_hat[t][k]
+ * (inferenceinterviews page, "A strong answer": divide activation channel j by
+ * s_j; katajob.com "Why are activations harder to quantize...", section
+ * "Activations are a distribution, not a tensor": dynamic per-token scales).
+ * X is read once.
+ *   X        device, x_t = SQ_F32 or SQ_BF16, [T][K]
+ *   s        device float [K], or NULL if X is already smoothed (for example
+ *            when 1/s was folded into the preceding normalisation gain)
+ *   Xq       device int8 [T][K], written;  x_scale  device float [T], written
+ */
+sq_status sq_quant_act(const void *X, sq_dtype x_t, int64_t T, int64_t K,
+                       const float *s, int8_t *Xq, float *x_scale, hipStream_t stream);
+
+/*
+ * W8A8 GEMM with int32 accumulation and the dequantising epilogue
+ * (mercemay.com "Activation Outlier Channels and Mixed-Precision Decomposition",
+ * section "Decomposition": integer matmul, float epilogue multiplying by the
+ * product of the two scales; maitreyasuin page, "Which scales factor out"):
+ *     acc[t][n] = sum_k Xq[t][k] * Wq[n][k]                (exact int32)
+ *     Y[t][n]   = fl32( fl32(acc[t][n]) * fl32(x_scale[t] * w_scale[n]) )
+ * y_t = SQ_F32 stores that value; SQ_BF16 stores it rounded to nearest-even
+ * bfloat16; SQ_I32 stores acc itself (x_scale and w_scale may then be NULL).
+ * Requires K <= SQ_MAX_K.
+ *   Xq  device int8 [T][K];  Wq  device int8 [N][K];  Y  device [T][N], written
+ */
+sq_status sq_w8a8_gemm(const int8_t *Xq, const float *x_scale,
+                       const int8_t *Wq, const float *w_scale,
+                       int64_t T, int64_t N, int64_t K, void *Y, sq_dtype y_t,
+                       hipStream_t stream);
+
+/* Bytes of device workspace sq_w8a8_linear needs for T tokens of width K
+ * (the int8 codes and the per-token scales, each 256-byte aligned). */
+size_t sq_w8a8_linear_workspace_size(int64_t T, int64_t K);
+
+/*
+ * The run-time layer: sq_quant_act of X with s into the workspace, then
+ * sq_w8a8_gemm against the prepared weights, on one stream.
+ *   X          device, x_t = SQ_F32 or SQ_BF16, [T][K]
+ *   s          device float [K] or NULL (as for sq_quant_act)
+ *   Wq, w_scale  from sq_quantize_weights
+ *   Y          device [T][N] of y_t = SQ_F32 or SQ_BF16, written
+ *   workspace  device memory of at least sq_w8a8_linear_workspace_size(T, K)
+ *              bytes, 256-byte aligned; the caller must not touch it until the
+ *              stream has passed this call
+ */
+sq_status sq_w8a8_linear(const void *X, sq_dtype x_t, const float *s,
+                         const int8_t *Wq, const float *w_scale,
+                         int64_t T, int64_t N, int64_t K, void *Y, sq_dtype y_t,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

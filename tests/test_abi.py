@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: libsq.so loads, exports every entry point that
+include/sq.h declares, and rejects bad arguments on the host before touching
+the device (these calls return before any HIP runtime call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "w8a8_quantized_amd", "libsq.so")
+HEADER = os.path.join(ROOT, "include", "sq.h")
+
+SQ_OK, SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALPHA, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP = range(7)
+F32, BF16, I32 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    L = ctypes.CDLL(LIB)
+    P, I64, F, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    L.sq_status_string.restype = ctypes.c_char_p
+    L.sq_status_string.argtypes = [I]
+    L.sq_col_absmax.argtypes = [P, I, I64, I64, P, I, P]
+    L.sq_smooth_scales_from_absmax.argtypes = [P, P, I64, F, P, P]
+    L.sq_smooth_scales.argtypes = [P, I, I64, P, I, I64, I64, F, P, P, P, P]
+    L.sq_quantize_weights.argtypes = [P, I, I64, I64, P, P, P, P]
+    L.sq_quant_act.argtypes = [P, I, I64, I64, P, P, P, P]
+    L.sq_w8a8_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+    L.sq_w8a8_linear_workspace_size.argtypes = [I64, I64]
+    L.sq_w8a8_linear_workspace_size.restype = ctypes.c_size_t
+    L.sq_w8a8_linear.argtypes = [P, I, P, P, P, I64, I64, I64, P, I, P, ctypes.c_size_t, P]
+    return L
+
+
+def test_header_declares_the_five_calls():
+    fns = declared_functions()
+    for name in ("sq_smooth_scales", "sq_quantize_weights", "sq_quant_act", "sq_w8a8_gemm",
+                 "sq_w8a8_linear"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_header():
+    src = open(os.path.join(ROOT, "w8a8_quantized_amd", "sq.py")).read()
+    for name in declared_functions():
+        assert re.search(rf"^def {name}\(", src, flags=re.M), name
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.sq_status_string(code).decode()
+        assert s.startswith("SQ_"), s
+    assert b"unknown" in lib.sq_status_string(99)
+
+
+# A fake non-NULL device address: validation fails before any use of it.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def test_null_pointers_rejected(lib):
+    assert lib.sq_col_absmax(None, F32, 4, 4, FAKE, 0, None) == SQ_ERR_NULL
+    assert lib.sq_col_absmax(FAKE, F32, 4, 4, None, 0, None) == SQ_ERR_NULL
+    assert lib.sq_quant_act(None, F32, 4, 4, None, FAKE, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_quant_act(FAKE, F32, 4, 4, None, None, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_quantize_weights(FAKE, F32, 4, 4, None, FAKE, None, None) == SQ_ERR_NULL
+    assert lib.sq_smooth_scales(FAKE, F32, 4, FAKE, F32, 4, 4, 0.5, FAKE, None, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_smooth_scales_from_absmax(FAKE, None, 4, 0.5, FAKE, None) == SQ_ERR_NULL
+    # scales are required unless the output is the raw int32 accumulator
+    assert lib.sq_w8a8_gemm(FAKE, None, FAKE, FAKE, 4, 4, 16, FAKE, F32, None) == SQ_ERR_NULL
+    assert lib.sq_w8a8_gemm(FAKE, FAKE, None, FAKE, 4, 4, 16, FAKE, I32, None) == SQ_ERR_NULL
+    assert lib.sq_w8a8_linear(FAKE, BF16, None, FAKE, None, 4, 4, 16, FAKE, BF16, FAKE, 1 << 20,
+                              None) == SQ_ERR_NULL
+
+
+def test_shapes_rejected(lib):
+    for r, c in ((0, 4), (4, 0), (-1, 4)):
+        assert lib.sq_col_absmax(FAKE, F32, r, c, FAKE, 0, None) == SQ_ERR_SHAPE
+        assert lib.sq_quant_act(FAKE, F32, r, c, None, FAKE, FAKE, None) == SQ_ERR_SHAPE
+        assert lib.sq_quantize_weights(FAKE, BF16, r, c, None, FAKE, FAKE, None) == SQ_ERR_SHAPE
+    assert lib.sq_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 16, FAKE, F32, None) == SQ_ERR_SHAPE
+    assert lib.sq_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 133145, FAKE, F32, None) == SQ_ERR_SHAPE
+    assert lib.sq_smooth_scales_from_absmax(FAKE, FAKE, 0, 0.5, FAKE, None) == SQ_ERR_SHAPE
+
+
+def test_alpha_rejected(lib):
+    for a in (-0.01, 1.01, float("nan"), float("inf")):
+        assert lib.sq_smooth_scales_from_absmax(FAKE, FAKE, 8, a, FAKE, None) == SQ_ERR_ALPHA
+        assert lib.sq_smooth_scales(FAKE, F32, 4, FAKE, F32, 4, 8, a, FAKE, FAKE, FAKE, None) == SQ_ERR_ALPHA
+
+
+def test_dtypes_rejected(lib):
+    assert lib.sq_col_absmax(FAKE, I32, 4, 4, FAKE, 0, None) == SQ_ERR_DTYPE
+    assert lib.sq_quant_act(FAKE, 7, 4, 4, None, FAKE, FAKE, None) == SQ_ERR_DTYPE
+    assert lib.sq_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 16, FAKE, 5, None) == SQ_ERR_DTYPE
+    # the linear layer produces floating-point outputs only
+    assert lib.sq_w8a8_linear(FAKE, F32, None, FAKE, FAKE, 4, 4, 16, FAKE, I32, FAKE, 1 << 20,
+                              None) == SQ_ERR_DTYPE
+
+
+def test_workspace(lib):
+    assert lib.sq_w8a8_linear_workspace_size(0, 4) == 0
+    assert lib.sq_w8a8_linear_workspace_size(3, 100) == 512 + 256
+    assert lib.sq_w8a8_linear_workspace_size(8192, 8192) == 8192 * 8192 + 8192 * 4
+    need = lib.sq_w8a8_linear_workspace_size(16, 64)
+    assert lib.sq_w8a8_linear(FAKE, F32, None, FAKE, FAKE, 16, 4, 64, FAKE, F32, FAKE, need - 1,
+                              None) == SQ_ERR_WORKSPACE
+    assert lib.sq_w8a8_linear(FAKE, F32, None, FAKE, FAKE, 16, 4, 64, FAKE, F32, None, need,
+                              None) == SQ_ERR_WORKSPACE
+    # workspace must be 256-byte aligned
+    assert lib.sq_w8a8_linear(FAKE, F32, None, FAKE, FAKE, 16, 4, 64, FAKE, F32,
+                              ctypes.c_void_p(0x1010), need, None) == SQ_ERR_WORKSPACE

@@ -1,0 +1,354 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar (identical inputs on both sides, seeded from workloads/):
+  * int8 codes, int32 accumulators, column maxima: bit-exact;
+  * x_scale / w_scale: bit-exact given the same smoothing factors s (the oracle is
+    fed the GPU's s); s itself within 1e-6 relative of the oracle's;
+  * fp32 outputs within 1e-5 relative, bf16 outputs within 2^-8 relative of the
+    oracle's fp32 output (and, since the epilogue order is fixed, equal to the
+    oracle's own fp32 and bf16 values).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import w8a8_quantized_amd as m   # raises if libsq.so is missing: no fallback
+    assert torch.cuda.is_available()
+    return m
+
+
+def dev_act(X, dtype):
+    """float32 numpy array (bf16-representable when dtype is bf16) -> device tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(X, np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+        assert torch.equal(t.float(), torch.from_numpy(np.ascontiguousarray(X, np.float32)))
+    return t.to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bf16_round(X):
+    return torch.from_numpy(np.ascontiguousarray(X, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def misaligned(t):
+    """Same values in a contiguous tensor whose data pointer is 4 bytes off a
+    16-byte boundary (forces the scalar kernels)."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    step = max(1, 4 // t.element_size())
+    v = flat[step:step + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0 and v.is_contiguous()
+    return v
+
+
+def assert_out_close(y_gpu, y_ref32, out):
+    """Contract tolerance against the oracle's fp32 output, plus equality with the
+    oracle's own rounding (same epilogue order)."""
+    if out == "f32":
+        assert np.array_equal(y_gpu, y_ref32)
+        assert np.all(np.abs(y_gpu - y_ref32) <= 1e-5 * np.abs(y_ref32))
+    else:
+        assert np.array_equal(y_gpu, O.to_bf16(y_ref32))
+        yf = O.widen_bf16(y_gpu).astype(np.float64)
+        r = y_ref32.astype(np.float64)
+        assert np.all(np.abs(yf - r) <= 2.0 ** -8 * np.abs(r))
+
+
+# ------------------------------------------------------------------ reductions
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(1, 1), (37, 80), (37, 83), (300, 1000), (1025, 8), (5000, 24)])
+def test_col_absmax(sq, dtype, rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    A = (rng.standard_normal((rows, cols)) * rng.uniform(0.1, 50, cols)).astype(np.float32)
+    if dtype == "bf16":
+        A = bf16_round(A)
+    A[rows // 2, cols // 3] = -1000.0
+    a = dev_act(A, dtype)
+    got = host(sq.sq_col_absmax(a))
+    assert np.array_equal(got, O.col_absmax(A))
+    if rows > 2:   # running maximum over two calls equals the maximum over all rows
+        m = sq.sq_col_absmax(a[: rows // 2].contiguous())
+        sq.sq_col_absmax(a[rows // 2:].contiguous(), amax=m, accumulate=True)
+        assert np.array_equal(host(m), O.col_absmax(A))
+    assert np.array_equal(host(sq.sq_col_absmax(misaligned(a))), O.col_absmax(A))
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.25, 0.5, 0.75, 1.0])
+def test_smooth_scales(sq, alpha):
+    w = WL.page_tiny_fixture(seed=3, T=50, N=70, K=96)
+    X = dev_act(w.X, "f32")
+    W = torch.from_numpy(w.W).to(DEV)
+    W[:, 5] = 0.0          # zero weight column and zero activation column: 1e-8 floor
+    X[:, 9] = 0.0
+    s, xa, wa = sq.sq_smooth_scales(X, W, alpha)
+    xa_r, wa_r = O.col_absmax(host(X)), O.col_absmax(host(W))
+    assert np.array_equal(host(xa), xa_r) and np.array_equal(host(wa), wa_r)
+    s_r = O.smooth_scales(xa_r, wa_r, alpha)
+    s_g = host(s)
+    if alpha in (0.0, 1.0):
+        assert np.array_equal(s_g, s_r)
+    np.testing.assert_allclose(s_g, s_r, rtol=1e-6, atol=0)
+    s2 = sq.sq_smooth_scales_from_absmax(xa, wa, alpha)
+    assert np.array_equal(host(s2), s_g)
+
+
+def test_smooth_scales_full_range(sq):
+    rng = np.random.default_rng(17)
+    xa = np.exp(rng.uniform(-25, 10, 200000)).astype(np.float32)
+    wa = np.exp(rng.uniform(-25, 5, 200000)).astype(np.float32)
+    xa[:10] = 0
+    wa[5:15] = 0
+    for alpha in (0.1, 0.5, 0.85):
+        s = sq.sq_smooth_scales_from_absmax(torch.from_numpy(xa).to(DEV), torch.from_numpy(wa).to(DEV), alpha)
+        np.testing.assert_allclose(host(s), O.smooth_scales(xa, wa, alpha), rtol=1e-6, atol=0)
+
+
+# ------------------------------------------------------------------ quantisers
+QSHAPES = [(1, 8), (37, 80), (5, 83), (64, 4096), (17, 16384), (3, 20000), (300, 1032), (2, 1)]
+
+
+def _special_rows(X):
+    X = X.copy()
+    X[0] = 0.0                                   # all-zero row: scale 1, codes 0
+    if X.shape[0] > 2 and X.shape[1] >= 8:
+        X[1] = -0.0
+        X[2, :] = 0.0
+        X[2, :5] = [127.0, 0.5, 1.5, 2.5, -2.5]  # ties (scale 1 when s is None)
+    return X
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_s", [False, True])
+@pytest.mark.parametrize("T,K", QSHAPES)
+def test_quant_act(sq, dtype, with_s, T, K):
+    rng = np.random.default_rng(T * 131 + K)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    X[:, rng.choice(K, max(1, K // 100), replace=False)] *= 40
+    X = _special_rows(X)
+    if dtype == "bf16":
+        X = bf16_round(X)
+    s = np.exp(rng.uniform(-3, 3, K)).astype(np.float32) if with_s else None
+    x = dev_act(X, dtype)
+    sd = torch.from_numpy(s).to(DEV) if with_s else None
+    Xq, xs = sq.sq_quant_act(x, sd)
+    Xq_r, xs_r = O.quant_act(X, s)
+    assert np.array_equal(host(xs), xs_r)
+    assert np.array_equal(host(Xq), Xq_r)
+    assert host(Xq).min() >= -127
+    if T > 2 and K >= 8 and not with_s:
+        assert host(Xq)[2, :5].tolist() == [127, 0, 2, 2, -2]
+    # the unaligned (scalar) kernel gives the same bits
+    Xq2, xs2 = sq.sq_quant_act(misaligned(x), sd)
+    assert np.array_equal(host(Xq2), Xq_r) and np.array_equal(host(xs2), xs_r)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_s", [False, True])
+@pytest.mark.parametrize("N,K", QSHAPES)
+def test_quantize_weights(sq, dtype, with_s, N, K):
+    rng = np.random.default_rng(N * 17 + K)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W = _special_rows(W)
+    if dtype == "bf16":
+        W = bf16_round(W)
+    s = np.exp(rng.uniform(-3, 3, K)).astype(np.float32) if with_s else None
+    w = dev_act(W, dtype)
+    sd = torch.from_numpy(s).to(DEV) if with_s else None
+    Wq, ws = sq.sq_quantize_weights(w, sd)
+    Wq_r, ws_r = O.quantize_weights(W, s)
+    assert np.array_equal(host(ws), ws_r)
+    assert np.array_equal(host(Wq), Wq_r)
+    Wq2, ws2 = sq.sq_quantize_weights(misaligned(w), sd)
+    assert np.array_equal(host(Wq2), Wq_r) and np.array_equal(host(ws2), ws_r)
+
+
+# ----------------------------------------------------------------------- GEMM
+def _codes(rng, r, k):
+    return rng.integers(-127, 128, (r, k), dtype=np.int8)
+
+
+GEMM_SHAPES = [
+    # decode kernel (T <= 64)
+    (1, 1, 16), (1, 40, 64), (5, 129, 80), (16, 1000, 256), (17, 77, 1040), (33, 64, 48), (64, 300, 528),
+    # prefill kernel, 128x128 tiles, ragged edges and K tails
+    (65, 40, 16), (100, 129, 64), (300, 1000, 80), (257, 513, 1040), (512, 1024, 4096),
+    # prefill kernel, 256x256 tiles (>= 256 tiles), ragged edges and a K tail
+    (2100, 8200, 48), (2048, 8192, 64),
+    # generic kernel (K % 16 != 0)
+    (3, 5, 7), (70, 33, 83), (1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
+def test_gemm_int32_accumulators(sq, T, N, K):
+    rng = np.random.default_rng(T * 1_000_003 + N * 101 + K)
+    Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)
+    acc = sq.sq_w8a8_gemm(torch.from_numpy(Xq).to(DEV), None, torch.from_numpy(Wq).to(DEV), None,
+                          out_dtype=torch.int32)
+    assert np.array_equal(host(acc), O.int_gemm(Xq, Wq))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("T,N,K", [(1, 40, 64), (17, 77, 1040), (300, 1000, 80), (2100, 8200, 48),
+                                   (70, 33, 83), (64, 130, 64), (129, 257, 64)])
+def test_gemm_epilogue(sq, out, T, N, K):
+    rng = np.random.default_rng(T + N + K)
+    Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)
+    xs = np.exp(rng.uniform(-8, 2, T)).astype(np.float32)
+    ws = np.exp(rng.uniform(-12, -2, N)).astype(np.float32)
+    y = sq.sq_w8a8_gemm(torch.from_numpy(Xq).to(DEV), torch.from_numpy(xs).to(DEV),
+                        torch.from_numpy(Wq).to(DEV), torch.from_numpy(ws).to(DEV),
+                        out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    y_r = O.dequant(O.int_gemm(Xq, Wq), xs, ws)
+    assert_out_close(host(y), y_r, out)
+
+
+def test_gemm_unaligned_output_row(sq):
+    """N % 4 != 0: element stores on the edge, same values."""
+    rng = np.random.default_rng(5)
+    for T, N, K in ((300, 1001, 64), (20, 1001, 64)):
+        Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)
+        xs = rng.uniform(0.01, 1, T).astype(np.float32)
+        ws = rng.uniform(0.001, 0.1, N).astype(np.float32)
+        y = sq.sq_w8a8_gemm(torch.from_numpy(Xq).to(DEV), torch.from_numpy(xs).to(DEV),
+                            torch.from_numpy(Wq).to(DEV), torch.from_numpy(ws).to(DEV),
+                            out_dtype=torch.bfloat16)
+        assert_out_close(host(y), O.dequant(O.int_gemm(Xq, Wq), xs, ws), "bf16")
+
+
+@pytest.mark.parametrize("T,K", [(2, 133136), (2, 133144), (80, 133136)])
+def test_gemm_int32_extremes(sq, T, K):
+    """|acc| up to 127^2 K at the largest K the contract allows (no overflow)."""
+    Xq = np.full((T, K), 127, np.int8)
+    Xq[1] = -127
+    Wq = np.full((3, K), 127, np.int8)
+    Wq[2] = -127
+    acc = host(sq.sq_w8a8_gemm(torch.from_numpy(Xq).to(DEV), None, torch.from_numpy(Wq).to(DEV),
+                               None, out_dtype=torch.int32))
+    assert acc[0, 0] == 127 * 127 * K and acc[1, 0] == -127 * 127 * K and acc[0, 2] == -127 * 127 * K
+    assert np.array_equal(acc, O.int_gemm(Xq, Wq))
+
+
+# ------------------------------------------------------------ linear end to end
+def _prepare_gpu(sq, w, alpha):
+    Xs = dev_act(w.stats_source, w.x_dtype)
+    W = torch.from_numpy(w.W).to(DEV)
+    s, xa, wa = sq.sq_smooth_scales(Xs, W, alpha)
+    Wq, ws = sq.sq_quantize_weights(W, s)
+    return s, xa, wa, Wq, ws
+
+
+def _check_prepare(w, alpha, s, xa, wa, Wq, ws):
+    xa_r, wa_r = O.col_absmax(w.stats_source), O.col_absmax(w.W)
+    assert np.array_equal(host(xa), xa_r) and np.array_equal(host(wa), wa_r)
+    s_g = host(s)
+    np.testing.assert_allclose(s_g, O.smooth_scales(xa_r, wa_r, alpha), rtol=1e-6, atol=0)
+    Wq_r, ws_r = O.quantize_weights(w.W, s_g)     # oracle fed the GPU's factors
+    assert np.array_equal(host(ws), ws_r)
+    assert np.array_equal(host(Wq), Wq_r)
+    return s_g, Wq_r, ws_r
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0])
+def test_linear_tiny_and_page(sq, alpha):
+    for name in ("tiny_t128_k1024_n1024", "page_t512_k4096_n4096"):
+        w = WL.make(name)
+        if alpha not in w.alphas and name.startswith("tiny"):
+            continue
+        s, xa, wa, Wq, ws = _prepare_gpu(sq, w, alpha)
+        s_g, Wq_r, ws_r = _check_prepare(w, alpha, s, xa, wa, Wq, ws)
+        X = dev_act(w.X, w.x_dtype)
+        y = sq.sq_w8a8_linear(X, s, Wq, ws, out_dtype=torch.float32)
+        Xq, xs = sq.sq_quant_act(X, s)
+        Xq_r, xs_r = O.quant_act(w.X, s_g)
+        assert np.array_equal(host(Xq), Xq_r) and np.array_equal(host(xs), xs_r)
+        acc = sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32)
+        acc_r = O.int_gemm(Xq_r, Wq_r)
+        assert np.array_equal(host(acc), acc_r)
+        assert_out_close(host(y), O.dequant(acc_r, xs_r, ws_r), "f32")
+
+
+def _sampled_pairs(rng, T, N, count):
+    ti = rng.integers(0, T, count)
+    ni = rng.integers(0, N, count)
+    # whole first/last rows and columns, and tile corners
+    edge_t = np.concatenate([np.zeros(N, np.int64), np.full(N, T - 1)])
+    edge_n = np.concatenate([np.arange(N), np.arange(N)])
+    col_t = np.concatenate([np.arange(T), np.arange(T)])
+    col_n = np.concatenate([np.zeros(T, np.int64), np.full(T, N - 1)])
+    return np.concatenate([ti, edge_t, col_t]), np.concatenate([ni, edge_n, col_n])
+
+
+@pytest.mark.parametrize("name", ["decode_t16_k8192_n28672", "prefill_t2048_k4096_n16384",
+                                  "heavy_t8192_k8192_n8192"])
+def test_linear_full_size(sq, name):
+    """Full-size workloads in the configuration the benchmark times: codes and
+    scales compared in full, accumulators and outputs on sampled (t, n) pairs
+    (all of them for the 16-token decode shape)."""
+    w = WL.make(name)
+    alpha = w.alpha
+    s, xa, wa, Wq, ws = _prepare_gpu(sq, w, alpha)
+    s_g, Wq_r, ws_r = _check_prepare(w, alpha, s, xa, wa, Wq, ws)
+    X = dev_act(w.X, w.x_dtype)
+    y = sq.sq_w8a8_linear(X, s, Wq, ws, out_dtype=torch.bfloat16)
+    Xq, xs = sq.sq_quant_act(X, s)
+    Xq_r, xs_r = O.quant_act(w.X, s_g)
+    assert np.array_equal(host(xs), xs_r)
+    assert np.array_equal(host(Xq), Xq_r)
+    yh = host(y)
+    if w.T <= 64:
+        acc_r = O.int_gemm(Xq_r, Wq_r)
+        acc = host(sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32))
+        assert np.array_equal(acc, acc_r)
+        assert_out_close(yh, O.dequant(acc_r, xs_r, ws_r), "bf16")
+    else:
+        rng = np.random.default_rng(42)
+        ti, ni = _sampled_pairs(rng, w.T, w.N, 200_000)
+        acc_r = O.int_gemm_at(Xq_r, Wq_r, ti, ni)
+        acc = host(sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32))
+        assert np.array_equal(acc[ti, ni], acc_r)
+        y_r = O.dequant_at(acc_r, xs_r, ws_r, ti, ni)
+        assert_out_close(yh[ti, ni], y_r, "bf16")
+    # the W8A8 layer actually tracks the exact product (smoothing worked)
+    rows = np.arange(0, w.T, max(1, w.T // 16))
+    ye = O.exact_product(w.X[rows], w.W)
+    err = np.linalg.norm(O.widen_bf16(yh[rows]) - ye) / np.linalg.norm(ye)
+    assert err < 0.05, err
+
+
+def test_linear_edge_cases(sq):
+    """T = 1, N = 1, K = 16, zero activation rows, zero weight rows."""
+    rng = np.random.default_rng(9)
+    for T, N, K in ((1, 1, 16), (1, 300, 64), (70, 1, 32), (3, 5, 16)):
+        X = rng.standard_normal((T, K)).astype(np.float32)
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        X[0] = 0.0
+        W[0] = 0.0
+        Xd, Wd = dev_act(X, "f32"), torch.from_numpy(W).to(DEV)
+        s, xa, wa = sq.sq_smooth_scales(Xd, Wd, 0.5)
+        Wq, ws = sq.sq_quantize_weights(Wd, s)
+        y = sq.sq_w8a8_linear(Xd, s, Wq, ws, out_dtype=torch.float32)
+        s_g = host(s)
+        Wq_r, ws_r = O.quantize_weights(W, s_g)
+        Xq_r, xs_r = O.quant_act(X, s_g)
+        y_r = O.dequant(O.int_gemm(Xq_r, Wq_r), xs_r, ws_r)
+        assert np.array_equal(host(Wq), Wq_r)
+        assert_out_close(host(y), y_r, "f32")
+        assert not host(y)[0].any() and not host(y)[:, 0].any()

@@ -1,0 +1,53 @@
+// Device helpers shared by the gfx950 kernels of the W8A8 layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kQmax = 127;   // symmetric int8 grid [-127, 127]
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// binary32 -> bfloat16, nearest with ties to even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (f != f) ? 0x7FC0u : r;
+}
+
+// Correctly rounded binary32 quotient a / b from a binary64 reciprocal:
+//   RN32(a / b) == (float)((double)a * rb)   with rb = RN64(1 / (double)b).
+// Why: a/b is never a binary32 rounding midpoint, and for 24-bit a and b it
+// stays at least 2^-49 (relative) away from every midpoint, while the binary64
+// product differs from a/b by less than 2^-51 (relative).  The two therefore
+// round to the same binary32 value.  Costs a multiply and two conversions in
+// place of the long IEEE division sequence.
+__device__ __forceinline__ float div_by_recip(float a, double rb) {
+  return (float)((double)a * rb);
+}
+
+// One int8 code of the symmetric quantiser: clamp(round_half_even(v / scale)).
+__device__ __forceinline__ int quant_code(float v, double rscale) {
+  float q = __builtin_rintf(div_by_recip(v, rscale));
+  q = __builtin_fminf(__builtin_fmaxf(q, -(float)kQmax), (float)kQmax);
+  return (int)q;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)d << 24);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace sq

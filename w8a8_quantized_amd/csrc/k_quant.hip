@@ -1,0 +1,226 @@
+// Row quantisers (gfx950): dynamic per-token activation quantisation fused with
+// the smoothing division, and per-output-channel weight quantisation fused with
+// the smoothing multiply.
+//
+// Both are the symmetric int8 round trip of maitreyasuin.github.io
+// "...01-one-outlier", section "The four operations" (scale = amax / 127, code =
+// clamp(round(v / scale), -127, 127), an all-zero row gets scale 1 and codes 0),
+// applied per row of X diag(s)^-1 (tokens) or of W diag(s) (output channels)
+// as on inferenceinterviews.com "Why do activation outliers break INT8 W8A8...",
+// section "A strong answer".
+//
+// Fast path (row length a multiple of 8, 16-byte aligned rows): a workgroup of 4
+// waves owns a fixed set of 8-element column chunks (chunk c = j*256 + thread)
+// and walks rows r = blockIdx.x, blockIdx.x + gridDim.x, ...  Per-column factors
+// (the binary64 reciprocal of s for the division, or s itself for the multiply)
+// therefore stay in registers across all of the workgroup's rows.  Each row is
+// read from HBM once, held in registers, reduced to its absmax (wave shuffle +
+// a 4-entry LDS exchange, one barrier), then turned into codes and written with
+// 8-byte stores.  The next row's loads are issued before the current row is
+// processed.  Both divisions of the method are done exactly as a multiply by a
+// binary64 reciprocal (see div_by_recip).
+//
+// Slow path (any shape/alignment): one workgroup per row, two passes over the
+// row with plain IEEE binary32 divisions; identical results.
+#include "common.h"
+#include "kernels.h"
+
+namespace sq {
+
+// 8 consecutive elements of one row as raw bits.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void unpack(float* o) const {
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void unpack(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+// Binary64 reciprocal accurate to ~1 ulp: hardware estimate + two Newton steps.
+// (The exactness argument of div_by_recip needs only a relative error < 2^-50.)
+__device__ __forceinline__ double recip64(double b) {
+  double y = __builtin_amdgcn_rcp(b);
+  double e = __builtin_fma(-b, y, 1.0);
+  y = __builtin_fma(y, e, y);
+  e = __builtin_fma(-b, y, 1.0);
+  return __builtin_fma(y, e, y);
+}
+
+// MODE: 0 = activations (divide by s), 1 = weights (multiply by s).
+template <typename T, int MODE, bool HAS_S, int CPT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A, int64_t R,
+                                                         int64_t K, const float* __restrict__ s,
+                                                         int8_t* __restrict__ Q,
+                                                         float* __restrict__ scale_out) {
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nchunks = K >> 3;
+
+  // per-column factors for the chunks this thread owns
+  double rs[CPT][8];   // MODE 0: 1 / s
+  float sv[CPT][8];    // MODE 1: s
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t c = (int64_t)j * 256 + tid;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float f = 1.0f;
+      if (HAS_S && c < nchunks) f = s[c * 8 + e];
+      if (MODE == 0) rs[j][e] = HAS_S ? recip64((double)f) : 1.0;
+      else sv[j][e] = f;
+    }
+  }
+
+  Raw8<T> cur[CPT], nxt[CPT];
+  int64_t r = blockIdx.x;
+  if (r < R) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t c = (int64_t)j * 256 + tid;
+      if (c < nchunks) cur[j].load(A + r * K + c * 8); else cur[j].zero();
+    }
+  }
+  int par = 0;
+  for (; r < R; r += gridDim.x) {
+    const int64_t rn = r + gridDim.x;
+    if (rn < R) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int64_t c = (int64_t)j * 256 + tid;
+        if (c < nchunks) nxt[j].load(A + rn * K + c * 8); else nxt[j].zero();
+      }
+    }
+    float v[CPT][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      float x[8];
+      cur[j].unpack(x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float h = x[e];
+        if (HAS_S) h = (MODE == 0) ? div_by_recip(x[e], rs[j][e]) : x[e] * sv[j][e];
+        v[j][e] = h;
+        m = fmaxf(m, fabsf(h));
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[par][wave] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
+    par ^= 1;
+    const float scale = amax == 0.0f ? 1.0f : amax / (float)kQmax;
+    const double rsc = 1.0 / (double)scale;
+    if (tid == 0) scale_out[r] = scale;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t c = (int64_t)j * 256 + tid;
+      if (c < nchunks) {
+        uint2 o;
+        o.x = pack4_i8(quant_code(v[j][0], rsc), quant_code(v[j][1], rsc), quant_code(v[j][2], rsc),
+                       quant_code(v[j][3], rsc));
+        o.y = pack4_i8(quant_code(v[j][4], rsc), quant_code(v[j][5], rsc), quant_code(v[j][6], rsc),
+                       quant_code(v[j][7], rsc));
+        *reinterpret_cast<uint2*>(Q + r * K + c * 8) = o;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) cur[j] = nxt[j];
+  }
+}
+
+// Any row length / alignment: one workgroup per row, plain binary32 divisions.
+template <typename T> __device__ __forceinline__ float load1(const T* p);
+template <> __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restrict__ A, int64_t R,
+                                                              int64_t K, const float* __restrict__ s,
+                                                              int8_t* __restrict__ Q,
+                                                              float* __restrict__ scale_out) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* row = A + r * K;
+    float m = 0.0f;
+    for (int64_t k = tid; k < K; k += 256) {
+      float x = load1<T>(row + k);
+      if (s) x = (MODE == 0) ? x / s[k] : x * s[k];
+      m = fmaxf(m, fabsf(x));
+    }
+    m = wave_max(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const float scale = amax == 0.0f ? 1.0f : amax / (float)kQmax;
+    if (tid == 0) scale_out[r] = scale;
+    for (int64_t k = tid; k < K; k += 256) {
+      float x = load1<T>(row + k);
+      if (s) x = (MODE == 0) ? x / s[k] : x * s[k];
+      float q = __builtin_rintf(x / scale);
+      q = fminf(fmaxf(q, -(float)kQmax), (float)kQmax);
+      Q[r * K + k] = (int8_t)(int)q;
+    }
+  }
+}
+
+template <typename T, int MODE, bool HAS_S>
+static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, int8_t* Q,
+                             float* scale, int ncu, hipStream_t st) {
+  const int64_t nchunks = K / 8;
+  const int cpt = (int)((nchunks + 255) / 256);
+  int64_t g = R < 3LL * ncu ? R : 3LL * ncu;
+  dim3 grid((unsigned)g), block(256);
+  switch (cpt) {
+    case 1: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 1>), grid, block, 0, st, A, R, K, s, Q, scale); break;
+    case 2: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 2>), grid, block, 0, st, A, R, K, s, Q, scale); break;
+    case 3:
+    case 4: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 4>), grid, block, 0, st, A, R, K, s, Q, scale); break;
+    default: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 8>), grid, block, 0, st, A, R, K, s, Q, scale); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int MODE>
+static hipError_t quant_dispatch(const T* A, int64_t R, int64_t K, const float* s, int8_t* Q,
+                                 float* scale, bool vec_ok, int ncu, hipStream_t st) {
+  if (vec_ok && K <= kQuantFastMaxK) {
+    return s ? quant_fast<T, MODE, true>(A, R, K, s, Q, scale, ncu, st)
+             : quant_fast<T, MODE, false>(A, R, K, s, Q, scale, ncu, st);
+  }
+  int64_t g = R < 8LL * ncu ? R : 8LL * ncu;
+  hipLaunchKernelGGL((quant_rows_slow_kernel<T, MODE>), dim3((unsigned)g), dim3(256), 0, st, A, R, K,
+                     s, Q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* A, bool bf16, bool weights, int64_t R, int64_t K,
+                             const float* s, int8_t* Q, float* scale, bool vec_ok, int ncu,
+                             hipStream_t st) {
+  if (bf16) {
+    const uint16_t* a = static_cast<const uint16_t*>(A);
+    return weights ? quant_dispatch<uint16_t, 1>(a, R, K, s, Q, scale, vec_ok, ncu, st)
+                   : quant_dispatch<uint16_t, 0>(a, R, K, s, Q, scale, vec_ok, ncu, st);
+  }
+  const float* a = static_cast<const float*>(A);
+  return weights ? quant_dispatch<float, 1>(a, R, K, s, Q, scale, vec_ok, ncu, st)
+                 : quant_dispatch<float, 0>(a, R, K, s, Q, scale, vec_ok, ncu, st);
+}
+
+}  // namespace sq

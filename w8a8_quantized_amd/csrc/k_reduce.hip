@@ -1,0 +1,163 @@
+// Column absolute maxima and smoothing factors (gfx950).
+//
+// Column absmax (inferenceinterviews.com "Why do activation outliers break INT8
+// W8A8...", section "A strong answer": max over tokens t of |X_tj| and over
+// output rows n of |W_nj|) is a pure HBM stream: each element is read once.
+// A workgroup is 4 waves; its 64 lanes each own one 16-byte column chunk and the
+// 4 waves walk interleaved rows of a row slab, so every wave load is 1 KB of one
+// row (fully coalesced).  The 4 partial maxima meet in LDS and one atomic max
+// per column and slab goes to the output.  |x| >= 0, so the unsigned order of
+// the binary32 bit patterns is the numeric order and an integer atomic max is
+// exact.
+#include "common.h"
+#include "kernels.h"
+
+namespace sq {
+
+__global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// Element loaders: VEC elements of one row starting at column c.
+template <typename T, int VEC> struct ChunkLoad;
+template <> struct ChunkLoad<float, 4> {
+  static __device__ __forceinline__ void abs(const float* p, float* o) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = fabsf(v.x); o[1] = fabsf(v.y); o[2] = fabsf(v.z); o[3] = fabsf(v.w);
+  }
+};
+template <> struct ChunkLoad<uint16_t, 8> {
+  static __device__ __forceinline__ void abs(const uint16_t* p, float* o) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = fabsf(bf16_lo(w[i]));
+      o[2 * i + 1] = fabsf(bf16_hi(w[i]));
+    }
+  }
+};
+template <> struct ChunkLoad<float, 1> {
+  static __device__ __forceinline__ void abs(const float* p, float* o) { o[0] = fabsf(*p); }
+};
+template <> struct ChunkLoad<uint16_t, 1> {
+  static __device__ __forceinline__ void abs(const uint16_t* p, float* o) { o[0] = fabsf(bf16_to_f32(*p)); }
+};
+
+// grid.x: groups of 64 chunks; grid.y: row slabs of `slab` rows.
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A, int64_t rows,
+                                                         int64_t cols, int64_t slab,
+                                                         float* __restrict__ amax) {
+  __shared__ float part[4][64][VEC];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * VEC;
+  const bool active = c0 < cols;   // cols % VEC == 0 on this path
+  const int64_t r_begin = (int64_t)blockIdx.y * slab;
+  const int64_t r_end = r_begin + slab < rows ? r_begin + slab : rows;
+  float m[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) m[i] = 0.0f;
+  if (active) {
+    const T* p = A + c0;
+    int64_t r = r_begin + wave;
+    // four rows in flight per wave
+    for (; r + 12 < r_end; r += 16) {
+      float a[4][VEC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ChunkLoad<T, VEC>::abs(p + (r + 4 * u) * cols, a[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) m[i] = fmaxf(m[i], a[u][i]);
+    }
+    for (; r < r_end; r += 4) {
+      float a[VEC];
+      ChunkLoad<T, VEC>::abs(p + r * cols, a);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) m[i] = fmaxf(m[i], a[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) part[wave][lane][i] = m[i];
+  __syncthreads();
+  if (wave == 0 && active) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      float v = fmaxf(fmaxf(part[0][lane][i], part[1][lane][i]),
+                      fmaxf(part[2][lane][i], part[3][lane][i]));
+      atomicMax(reinterpret_cast<unsigned int*>(amax + c0 + i), __float_as_uint(v));
+    }
+  }
+}
+
+// s_j = max(xa_j, 1e-8)^alpha / max(wa_j, 1e-8)^(1 - alpha), binary64, rounded once
+// (multigrid.ai "SmoothQuant Explained", section "Alpha: how much difficulty to
+// move"; 1e-8 floor from the maitreyasuin page, section "Route it, or move it").
+__global__ void smooth_scales_kernel(const float* __restrict__ xa, const float* __restrict__ wa,
+                                     int64_t K, double alpha, float* __restrict__ s) {
+  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  const float eps = 1e-8f;
+  const float x = xa[j] < eps ? eps : xa[j];
+  const float w = wa[j] < eps ? eps : wa[j];
+  double r;
+  if (alpha == 0.0) {
+    r = 1.0 / (double)w;                 // the alpha = 0 form, exactly
+  } else if (alpha == 1.0) {
+    r = (double)x;                       // the alpha = 1 form, exactly
+  } else {
+    r = pow((double)x, alpha) / pow((double)w, 1.0 - alpha);
+  }
+  s[j] = (float)r;
+}
+
+static int grid_1d(int64_t n, int threads, int cap) {
+  int64_t g = (n + threads - 1) / threads;
+  return (int)(g < cap ? (g < 1 ? 1 : g) : cap);
+}
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_1d(n, 256, 1024)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+template <typename T, int VEC>
+static hipError_t col_absmax_t(const T* A, int64_t rows, int64_t cols, float* amax, int ncu,
+                               hipStream_t st) {
+  const int64_t chunks = (cols + VEC - 1) / VEC;
+  const int64_t gx = (chunks + 63) / 64;
+  const int64_t target = 8LL * ncu;                 // workgroups to fill the chip
+  int64_t slabs = target / gx;
+  if (slabs < 1) slabs = 1;
+  int64_t max_slabs = (rows + 15) / 16;             // at least 16 rows per slab
+  if (slabs > max_slabs) slabs = max_slabs;
+  if (slabs > 65535) slabs = 65535;
+  int64_t slab = (rows + slabs - 1) / slabs;
+  slabs = (rows + slab - 1) / slab;
+  hipLaunchKernelGGL((col_absmax_kernel<T, VEC>), dim3((unsigned)gx, (unsigned)slabs), dim3(256), 0,
+                     st, A, rows, cols, slab, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, float* amax,
+                             bool vec_ok, int ncu, hipStream_t st) {
+  if (bf16) {
+    const uint16_t* a = static_cast<const uint16_t*>(A);
+    return vec_ok ? col_absmax_t<uint16_t, 8>(a, rows, cols, amax, ncu, st)
+                  : col_absmax_t<uint16_t, 1>(a, rows, cols, amax, ncu, st);
+  }
+  const float* a = static_cast<const float*>(A);
+  return vec_ok ? col_absmax_t<float, 4>(a, rows, cols, amax, ncu, st)
+                : col_absmax_t<float, 1>(a, rows, cols, amax, ncu, st);
+}
+
+hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(smooth_scales_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, xa,
+                     wa, K, (double)alpha, s);
+  return hipGetLastError();
+}
+
+}  // namespace sq

@@ -1,0 +1,44 @@
+// Internal launchers of the gfx950 kernels (host side).  Arguments are already
+// validated by the C ABI layer; every launcher returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+// Largest row length the register-resident quantiser handles (256 threads x
+// 8 elements x 8 chunks); longer rows take the two-pass kernel.
+constexpr int64_t kQuantFastMaxK = 16384;
+
+enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, float* amax,
+                             bool vec_ok, int ncu, hipStream_t st);
+hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
+                                hipStream_t st);
+hipError_t launch_quant_rows(const void* A, bool bf16, bool weights, int64_t R, int64_t K,
+                             const float* s, int8_t* Q, float* scale, bool vec_ok, int ncu,
+                             hipStream_t st);
+
+struct GemmArgs {
+  const int8_t* Xq;
+  const float* xs;
+  const int8_t* Wq;
+  const float* ws;
+  int64_t T, N, K;
+  void* Y;
+  int out;          // OutKind
+  bool vec_store;   // Y rows allow 8/16-byte stores (N % 4 == 0, aligned base)
+};
+
+// Prefill-shaped GEMM on the int8 MFMA units (K % 16 == 0, 16-byte aligned operands).
+hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st);
+// Decode-shaped skinny GEMM (T <= 64; K % 16 == 0, 16-byte aligned operands).
+hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st);
+// Any shape and alignment (one thread per output, scalar loads).
+hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st);
+
+constexpr int64_t kDecodeMaxT = 64;
+
+}  // namespace sq

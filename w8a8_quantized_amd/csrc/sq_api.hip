@@ -1,0 +1,166 @@
+// C ABI of the W8A8 layer: argument validation, kernel selection, launches.
+// The semantics of each entry point are documented in include/sq.h.
+#include <atomic>
+#include <cmath>
+
+#include "../../include/sq.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_ncu[kMaxDevices];   // 0 = not queried yet
+
+// Compute units of the current device (cached; falls back to 256 if the query fails).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_ncu[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_ncu[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool in_dtype(sq_dtype t) { return t == SQ_F32 || t == SQ_BF16; }
+size_t esize(sq_dtype t) { return t == SQ_BF16 ? 2 : 4; }
+
+// Rows of `cols` elements starting at p can be read as 16-byte chunks.
+bool rows_vec16(const void* p, int64_t cols, size_t es) {
+  return aligned16(p) && ((uint64_t)cols * es) % 16 == 0;
+}
+
+sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+sq_status check_gemm_args(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
+                          int64_t T, int64_t N, int64_t K, const void* Y, sq_dtype y_t) {
+  if (!Xq || !Wq || !Y) return SQ_ERR_NULL;
+  if (y_t != SQ_F32 && y_t != SQ_BF16 && y_t != SQ_I32) return SQ_ERR_DTYPE;
+  if (y_t != SQ_I32 && (!xs || !ws)) return SQ_ERR_NULL;
+  if (T < 1 || N < 1 || K < 1 || K > SQ_MAX_K) return SQ_ERR_SHAPE;
+  return SQ_OK;
+}
+
+sq_status run_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int64_t T,
+                   int64_t N, int64_t K, void* Y, sq_dtype y_t, hipStream_t st) {
+  sq::GemmArgs a;
+  a.Xq = Xq; a.xs = xs; a.Wq = Wq; a.ws = ws;
+  a.T = T; a.N = N; a.K = K; a.Y = Y;
+  a.out = y_t == SQ_F32 ? sq::kOutF32 : (y_t == SQ_BF16 ? sq::kOutBF16 : sq::kOutI32);
+  a.vec_store = (N % 4 == 0) && aligned16(Y) && (y_t == SQ_I32 || aligned16(ws));
+  const bool mfma_ok = (K % 16 == 0) && aligned16(Xq) && aligned16(Wq);
+  if (!mfma_ok) return hip_status(sq::launch_gemm_generic(a, st));
+  if (T <= sq::kDecodeMaxT) return hip_status(sq::launch_gemv_mfma(a, cu_count(), st));
+  return hip_status(sq::launch_gemm_mfma(a, cu_count(), st));
+}
+
+sq_status run_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
+                        int8_t* Xq, float* xs, hipStream_t st) {
+  const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
+  return hip_status(
+      sq::launch_quant_rows(X, x_t == SQ_BF16, false, T, K, s, Xq, xs, vec, cu_count(), st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sq_status_string(sq_status status) {
+  switch (status) {
+    case SQ_OK: return "SQ_OK: success";
+    case SQ_ERR_NULL: return "SQ_ERR_NULL: a required pointer is NULL";
+    case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: a size is < 1 or K exceeds SQ_MAX_K";
+    case SQ_ERR_ALPHA: return "SQ_ERR_ALPHA: alpha is NaN or outside [0, 1]";
+    case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: dtype not accepted for this argument";
+    case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
+    case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown sq_status";
+}
+
+sq_status sq_col_absmax(const void* A, sq_dtype a_t, int64_t rows, int64_t cols, float* amax,
+                        int accumulate, hipStream_t stream) {
+  if (!A || !amax) return SQ_ERR_NULL;
+  if (!in_dtype(a_t)) return SQ_ERR_DTYPE;
+  if (rows < 1 || cols < 1) return SQ_ERR_SHAPE;
+  if (!accumulate) {
+    if (sq::launch_fill(amax, cols, 0.0f, stream) != hipSuccess) return SQ_ERR_HIP;
+  }
+  const bool vec = rows_vec16(A, cols, esize(a_t));
+  return hip_status(sq::launch_col_absmax(A, a_t == SQ_BF16, rows, cols, amax, vec, cu_count(), stream));
+}
+
+sq_status sq_smooth_scales_from_absmax(const float* x_absmax, const float* w_absmax, int64_t K,
+                                       float alpha, float* s, hipStream_t stream) {
+  if (!x_absmax || !w_absmax || !s) return SQ_ERR_NULL;
+  if (K < 1) return SQ_ERR_SHAPE;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+  return hip_status(sq::launch_smooth_scales(x_absmax, w_absmax, K, alpha, s, stream));
+}
+
+sq_status sq_smooth_scales(const void* X, sq_dtype x_t, int64_t T, const void* W, sq_dtype w_t,
+                           int64_t N, int64_t K, float alpha, float* s, float* x_absmax,
+                           float* w_absmax, hipStream_t stream) {
+  if (!X || !W || !s || !x_absmax || !w_absmax) return SQ_ERR_NULL;
+  if (!in_dtype(x_t) || !in_dtype(w_t)) return SQ_ERR_DTYPE;
+  if (T < 1 || N < 1 || K < 1) return SQ_ERR_SHAPE;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+  sq_status r = sq_col_absmax(X, x_t, T, K, x_absmax, 0, stream);
+  if (r != SQ_OK) return r;
+  r = sq_col_absmax(W, w_t, N, K, w_absmax, 0, stream);
+  if (r != SQ_OK) return r;
+  return sq_smooth_scales_from_absmax(x_absmax, w_absmax, K, alpha, s, stream);
+}
+
+sq_status sq_quantize_weights(const void* W, sq_dtype w_t, int64_t N, int64_t K, const float* s,
+                              int8_t* Wq, float* w_scale, hipStream_t stream) {
+  if (!W || !Wq || !w_scale) return SQ_ERR_NULL;
+  if (!in_dtype(w_t)) return SQ_ERR_DTYPE;
+  if (N < 1 || K < 1) return SQ_ERR_SHAPE;
+  const bool vec = (K % 8 == 0) && rows_vec16(W, K, esize(w_t)) && aligned16(Wq);
+  return hip_status(
+      sq::launch_quant_rows(W, w_t == SQ_BF16, true, N, K, s, Wq, w_scale, vec, cu_count(), stream));
+}
+
+sq_status sq_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s, int8_t* Xq,
+                       float* x_scale, hipStream_t stream) {
+  if (!X || !Xq || !x_scale) return SQ_ERR_NULL;
+  if (!in_dtype(x_t)) return SQ_ERR_DTYPE;
+  if (T < 1 || K < 1) return SQ_ERR_SHAPE;
+  return run_quant_act(X, x_t, T, K, s, Xq, x_scale, stream);
+}
+
+sq_status sq_w8a8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                       int64_t T, int64_t N, int64_t K, void* Y, sq_dtype y_t, hipStream_t stream) {
+  sq_status r = check_gemm_args(Xq, x_scale, Wq, w_scale, T, N, K, Y, y_t);
+  if (r != SQ_OK) return r;
+  return run_gemm(Xq, x_scale, Wq, w_scale, T, N, K, Y, y_t, stream);
+}
+
+size_t sq_w8a8_linear_workspace_size(int64_t T, int64_t K) {
+  if (T < 1 || K < 1) return 0;
+  return round256((size_t)T * (size_t)K) + round256((size_t)T * sizeof(float));
+}
+
+sq_status sq_w8a8_linear(const void* X, sq_dtype x_t, const float* s, const int8_t* Wq,
+                         const float* w_scale, int64_t T, int64_t N, int64_t K, void* Y, sq_dtype y_t,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+  if (!in_dtype(x_t) || !in_dtype(y_t)) return SQ_ERR_DTYPE;
+  if (T < 1 || N < 1 || K < 1 || K > SQ_MAX_K) return SQ_ERR_SHAPE;
+  if (!workspace || workspace_bytes < sq_w8a8_linear_workspace_size(T, K) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SQ_ERR_WORKSPACE;
+  int8_t* Xq = static_cast<int8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)T * (size_t)K));
+  sq_status r = run_quant_act(X, x_t, T, K, s, Xq, xs, stream);
+  if (r != SQ_OK) return r;
+  return run_gemm(Xq, xs, Wq, w_scale, T, N, K, Y, y_t, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+"""Python binding of libsq.so (include/sq.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors are torch
+tensors on the current HIP device (PyTorch provides the device memory and the
+stream; all arithmetic runs in the library's kernels).  Outputs that are not
+passed in are allocated with torch.empty.  A non-OK status raises RuntimeError
+with the library's status string.  There is no fallback: if libsq.so is missing
+the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsq.so")
+
+SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
+SQ_MAX_K = 133144
+_DT = {torch.float32: SQ_F32, torch.bfloat16: SQ_BF16, torch.int32: SQ_I32}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m w8a8_quantized_amd.build` "
+                      "(or __graft_entry__.build())")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I64, _F, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "sq_status_string": ([_I], ctypes.c_char_p),
+    "sq_col_absmax": ([_P, _I, _I64, _I64, _P, _I, _P], _I),
+    "sq_smooth_scales_from_absmax": ([_P, _P, _I64, _F, _P, _P], _I),
+    "sq_smooth_scales": ([_P, _I, _I64, _P, _I, _I64, _I64, _F, _P, _P, _P, _P], _I),
+    "sq_quantize_weights": ([_P, _I, _I64, _I64, _P, _P, _P, _P], _I),
+    "sq_quant_act": ([_P, _I, _I64, _I64, _P, _P, _P, _P], _I),
+    "sq_w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
+    "sq_w8a8_linear_workspace_size": ([_I64, _I64], _SZ),
+    "sq_w8a8_linear": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+def sq_status_string(status: int) -> str:
+    return _lib.sq_status_string(int(status)).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError(sq_status_string(rc))
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t, allowed=(torch.float32, torch.bfloat16)):
+    if t.dtype not in allowed:
+        raise ValueError(f"dtype {t.dtype} not accepted (expected one of {allowed})")
+    return _DT[t.dtype]
+
+
+def _want(t, shape, dtype, dev):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"output must be {dtype} of shape {tuple(shape)}")
+    return t
+
+
+def sq_col_absmax(A, amax=None, accumulate=False):
+    """amax[j] = max_i |A[i, j]| (running max if accumulate)."""
+    rows, cols = A.shape
+    amax = _want(amax, (cols,), torch.float32, A.device)
+    _check(_lib.sq_col_absmax(_ptr(A), _dt(A), rows, cols, _ptr(amax), int(bool(accumulate)),
+                              _stream(A.device)))
+    return amax
+
+
+def sq_smooth_scales_from_absmax(x_absmax, w_absmax, alpha, s=None):
+    """s = max(xa,1e-8)^alpha / max(wa,1e-8)^(1-alpha)."""
+    K = x_absmax.numel()
+    if w_absmax.numel() != K:
+        raise ValueError("x_absmax and w_absmax differ in length")
+    s = _want(s, (K,), torch.float32, x_absmax.device)
+    _check(_lib.sq_smooth_scales_from_absmax(_ptr(x_absmax), _ptr(w_absmax), K, float(alpha),
+                                             _ptr(s), _stream(x_absmax.device)))
+    return s
+
+
+def sq_smooth_scales(X, W, alpha, s=None, x_absmax=None, w_absmax=None):
+    """Smoothing factors from a calibration batch X [T, K] and weights W [N, K].
+    Returns (s, x_absmax, w_absmax)."""
+    T, K = X.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError("X and W differ in K")
+    dev = X.device
+    s = _want(s, (K,), torch.float32, dev)
+    x_absmax = _want(x_absmax, (K,), torch.float32, dev)
+    w_absmax = _want(w_absmax, (K,), torch.float32, dev)
+    _check(_lib.sq_smooth_scales(_ptr(X), _dt(X), T, _ptr(W), _dt(W), N, K, float(alpha), _ptr(s),
+                                 _ptr(x_absmax), _ptr(w_absmax), _stream(dev)))
+    return s, x_absmax, w_absmax
+
+
+def sq_quantize_weights(W, s=None, Wq=None, w_scale=None):
+    """Per-output-channel int8 weights of W diag(s).  Returns (Wq, w_scale)."""
+    N, K = W.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    Wq = _want(Wq, (N, K), torch.int8, W.device)
+    w_scale = _want(w_scale, (N,), torch.float32, W.device)
+    _check(_lib.sq_quantize_weights(_ptr(W), _dt(W), N, K, _ptr(s), _ptr(Wq), _ptr(w_scale),
+                                    _stream(W.device)))
+    return Wq, w_scale
+
+
+def sq_quant_act(X, s=None, Xq=None, x_scale=None):
+    """Dynamic per-token int8 codes of X diag(s)^-1.  Returns (Xq, x_scale)."""
+    T, K = X.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    Xq = _want(Xq, (T, K), torch.int8, X.device)
+    x_scale = _want(x_scale, (T,), torch.float32, X.device)
+    _check(_lib.sq_quant_act(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(Xq), _ptr(x_scale),
+                             _stream(X.device)))
+    return Xq, x_scale
+
+
+def sq_w8a8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
+    """Y = dequant(Xq @ Wq^T); out_dtype torch.int32 returns the raw accumulators."""
+    T, K = Xq.shape
+    N, K2 = Wq.shape
+    if K != K2 or Xq.dtype != torch.int8 or Wq.dtype != torch.int8:
+        raise ValueError("Xq [T, K] and Wq [N, K] must be int8 with the same K")
+    yt = _DT.get(out_dtype)
+    if yt is None:
+        raise ValueError(f"out_dtype {out_dtype} not accepted")
+    Y = _want(Y, (T, N), out_dtype, Xq.device)
+    _check(_lib.sq_w8a8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), T, N, K, _ptr(Y),
+                             yt, _stream(Xq.device)))
+    return Y
+
+
+def sq_w8a8_linear_workspace_size(T, K):
+    return int(_lib.sq_w8a8_linear_workspace_size(int(T), int(K)))
+
+
+def sq_w8a8_linear(X, s, Wq, w_scale, out_dtype=torch.bfloat16, Y=None, workspace=None):
+    """Run-time layer: per-token quantisation of X diag(s)^-1, then the W8A8 GEMM."""
+    T, K = X.shape
+    N, K2 = Wq.shape
+    if K != K2:
+        raise ValueError("X and Wq differ in K")
+    yt = _DT.get(out_dtype)
+    if yt is None or out_dtype == torch.int32:
+        raise ValueError(f"out_dtype {out_dtype} not accepted")
+    Y = _want(Y, (T, N), out_dtype, X.device)
+    need = sq_w8a8_linear_workspace_size(T, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _check(_lib.sq_w8a8_linear(_ptr(X), _dt(X), _ptr(s), _ptr(Wq), _ptr(w_scale), T, N, K, _ptr(Y),
+                               yt, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(X.device)))
+    return Y
