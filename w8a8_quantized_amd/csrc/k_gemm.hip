@@ -75,69 +75,101 @@ __device__ __forceinline__ void tile_coords(int bid, int G, int tiles_n, int til
   tt = within / gn;
 }
 
+// s_waitcnt immediate for "vmcnt <= n" (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt 6:4 left at 7; lgkmcnt 11:8 at 15, or at 0 with kLgkm0).
+constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+constexpr int kLgkm0 = ~0x0F00;
+
 // Requires K % 16 == 0, (N + BN) * K < 2^31 and (T + BT) * K < 2^31 (the host
 // splits larger problems), 16-byte aligned Xq and Wq.
-template <int BN, int BT, int BK, int WN, int WT, int OUT, bool VEC>
+//
+// Main loop.  A STAGES-deep ring of LDS stages, each holding BN rows of Wq and
+// BT rows of Xq, BK bytes wide.  Stages are filled by direct-to-LDS buffer loads
+// (one 1 KB wave instruction per 64/CPR rows: lane l deposits 16 bytes at
+// slot l of the instruction's 1 KB block, so each lane fetches the logical
+// chunk that belongs at its slot under the XOR swizzle).  Fragments of step q+1
+// are read from LDS while the MFMAs of step q run; the per-stage barrier sits
+// after half of the last step's MFMAs.  The barrier is a bare s_barrier
+// preceded by this wave's own "vmcnt <= loads of later stages" wait: a fenced
+// barrier would also wait for the later stages still in flight.
+//
+// Epilogue (VEC).  Each wave stages 32 token rows x WTN outputs at a time in
+// LDS (rows padded by 16 bytes) and writes them back as row-contiguous 16-byte
+// stores, so every store instruction covers whole 256/512-byte row segments.
+template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC>
 __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy,
     int tiles_n, int tiles_t) {
-  constexpr int NT = WN * WT * 64;
+  // The body exists only in the device pass (the host pass needs just the
+  // launch stub, and its front end cannot take the device scheduling builtins).
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = WN * WT;
   constexpr int CPR = BK / 16;                 // 16-byte chunks per LDS row
-  constexpr int RPB = 16 / CPR;                // LDS rows per 256-byte bank line
-  constexpr int RSTEP = NT / CPR;              // rows covered by one staging pass
+  constexpr int RPB = 16 / CPR;                // rows sharing one 256-byte bank line
+  constexpr int ROWS_PER_INSN = 64 / CPR;      // rows one wave-wide DMA load covers
   constexpr int WTN = BN / WN, WTT = BT / WT;  // wave tile
   constexpr int RN = WTN / 32, RT = WTT / 32;  // 32x32 MFMA blocks per wave
-  constexpr int A_LD = BN / RSTEP, B_LD = BT / RSTEP;
-  static_assert(A_LD * RSTEP == BN && B_LD * RSTEP == BT && RSTEP % 16 == 0, "tile/threads mismatch");
-  __shared__ __attribute__((aligned(16))) int8_t lds[2][(BN + BT) * BK];
+  constexpr int KK = BK / 32;                  // MFMA k-steps per stage
+  constexpr int A_INSN = BN / ROWS_PER_INSN / NW, B_INSN = BT / ROWS_PER_INSN / NW;
+  constexpr int STAGE_BYTES = (BN + BT) * BK;
+  constexpr int PER = A_INSN + B_INSN;         // DMA loads per stage per wave
+  static_assert(A_INSN * ROWS_PER_INSN * NW == BN && B_INSN * ROWS_PER_INSN * NW == BT, "tile/waves");
+  static_assert(KK % 2 == 0 && STAGES >= 2, "pipeline shape");
+  __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
 
   int tn, tt;
   tile_coords(blockIdx.x, gridDim.x, tiles_n, tiles_t, tn, tt);
   const int n0 = tn * BN, t0 = tt * BT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wt = wave / WN;
-
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Wq, N * K);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Xq, T * K);
 
-  // staging: this thread moves chunk c of rows r0 + p*RSTEP (p < A_LD / B_LD)
-  const int c = tid % CPR, r0 = tid / CPR;
-  const int a_goff = (n0 + r0) * K + c * 16;
-  const int b_goff = (t0 + r0) * K + c * 16;
-  const int st_off = r0 * BK + ((c ^ ((r0 / RPB) % CPR)) * 16);   // same swizzle for every p
-
+  // DMA source offsets: LDS row r of an instruction block, physical chunk pc,
+  // holds logical chunk pc ^ swz(r).
+  const int lrow = lane / CPR, pc = lane % CPR;
+  int a_off[A_INSN], b_off[B_INSN], a_ch[A_INSN], b_ch[B_INSN];
+#pragma unroll
+  for (int p = 0; p < A_INSN; ++p) {
+    const int row = (wave * A_INSN + p) * ROWS_PER_INSN + lrow;
+    a_ch[p] = (pc ^ ((row / RPB) % CPR)) * 16;
+    a_off[p] = (n0 + row) * K + a_ch[p];
+  }
+#pragma unroll
+  for (int p = 0; p < B_INSN; ++p) {
+    const int row = (wave * B_INSN + p) * ROWS_PER_INSN + lrow;
+    b_ch[p] = (pc ^ ((row / RPB) % CPR)) * 16;
+    b_off[p] = (t0 + row) * K + b_ch[p];
+  }
   // The whole byte offset goes in the VGPR operand: the buffer range check
   // covers that operand (not the scalar one), so rows past the edge and masked
-  // K-tail chunks (sent to kOob) read as zero and never leave the allocation.
+  // K-tail chunks (sent to kOob) arrive as zeros and never leave the allocation.
   constexpr int kOob = 0x7FFFFFF0;
-  v4i ra[A_LD], rb[B_LD];
-  auto gload = [&](int k0) {
-    const bool kin = c * 16 < K - k0;   // false only in a partial last K stage
+  auto issue = [&](int buf, int k0) {
+    int8_t* L = lds + buf * STAGE_BYTES;
+    const int kv = K - k0;
 #pragma unroll
-    for (int p = 0; p < A_LD; ++p)
-      ra[p] = __builtin_amdgcn_raw_buffer_load_b128(rsA, kin ? a_goff + p * RSTEP * K + k0 : kOob, 0, 0);
+    for (int p = 0; p < A_INSN; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (__attribute__((address_space(3))) void*)(L + (wave * A_INSN + p) * 1024), 16,
+          a_ch[p] < kv ? a_off[p] + k0 : kOob, 0, 0, 0);
 #pragma unroll
-    for (int p = 0; p < B_LD; ++p)
-      rb[p] = __builtin_amdgcn_raw_buffer_load_b128(rsB, kin ? b_goff + p * RSTEP * K + k0 : kOob, 0, 0);
-  };
-  auto lstore = [&](int buf) {
-    int8_t* base = &lds[buf][st_off];
-#pragma unroll
-    for (int p = 0; p < A_LD; ++p) *reinterpret_cast<v4i*>(base + p * RSTEP * BK) = ra[p];
-#pragma unroll
-    for (int p = 0; p < B_LD; ++p) *reinterpret_cast<v4i*>(base + BN * BK + p * RSTEP * BK) = rb[p];
+    for (int p = 0; p < B_INSN; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (__attribute__((address_space(3))) void*)(L + BN * BK + (wave * B_INSN + p) * 1024), 16,
+          b_ch[p] < kv ? b_off[p] + k0 : kOob, 0, 0, 0);
   };
 
-  // fragment reads: rows wn*WTN + i*32 + fr (A) and wt*WTT + j*32 + fr (B); the
-  // block offsets are multiples of 16 rows, so the swizzle depends on fr only
+  // Fragment reads: rows wn*WTN + i*32 + fr (A) and wt*WTT + j*32 + fr (B).  The
+  // block offsets are multiples of 16 rows, so the swizzle depends on fr only.
   const int fr = lane & 31, fc = lane >> 5;
   const int sw = (fr / RPB) % CPR;
   const int a_base = (wn * WTN + fr) * BK;
   const int b_base = BN * BK + (wt * WTT + fr) * BK;
-  int cofs[BK / 32];
+  int cofs[KK];
 #pragma unroll
-  for (int kk = 0; kk < BK / 32; ++kk) cofs[kk] = ((kk * 2 + fc) ^ sw) * 16;
+  for (int kk = 0; kk < KK; ++kk) cofs[kk] = ((kk * 2 + fc) ^ sw) * 16;
 
   v16i acc[RN][RT];
 #pragma unroll
@@ -145,89 +177,184 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < RT; ++j) acc[i][j] = v16i{};
 
-  const int nst = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nst) gload((s + 1) * BK);
-    const int8_t* L = &lds[cur][0];
+  v4i fa[2][RN], fb[2][RT];
+  auto read_frags = [&](int slot, const int8_t* L, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      v4i fa[RN], fb[RT];
+    for (int i = 0; i < RN; ++i) fa[slot][i] = *reinterpret_cast<const v4i*>(L + a_base + cofs[kk] + i * 32 * BK);
 #pragma unroll
-      for (int i = 0; i < RN; ++i)
-        fa[i] = *reinterpret_cast<const v4i*>(L + a_base + cofs[kk] + i * 32 * BK);
+    for (int j = 0; j < RT; ++j) fb[slot][j] = *reinterpret_cast<const v4i*>(L + b_base + cofs[kk] + j * 32 * BK);
+  };
+  auto mfmas = [&](int slot, int first, int count) {
 #pragma unroll
-      for (int j = 0; j < RT; ++j)
-        fb[j] = *reinterpret_cast<const v4i*>(L + b_base + cofs[kk] + j * 32 * BK);
-#pragma unroll
-      for (int i = 0; i < RN; ++i)
-#pragma unroll
-        for (int j = 0; j < RT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < RN * RT; ++q) {
+      if (q < first || q >= first + count) continue;
+      const int i = q / RT, j = q % RT;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < nst) lstore(cur ^ 1);
-    __syncthreads();
+  };
+  // wait until at most `later` stages of this wave's DMA loads are in flight
+  // (and, for wait_vm_lds, its LDS reads are complete)
+  auto wait_vm = [&](int later) {
+    if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_enc(3 * PER));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * PER));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(PER));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+  };
+  auto wait_vm_lds = [&](int later) {
+    if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_enc(3 * PER) & kLgkm0);
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * PER) & kLgkm0);
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(PER) & kLgkm0);
+    else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0) & kLgkm0);
+  };
+  auto bar = [&] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int nst = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nst) issue(s, s * BK);
+  wait_vm(nst - 1 < STAGES - 1 ? nst - 1 : STAGES - 1);
+  bar();
+  read_frags(0, lds, 0);
+
+  for (int s = 0; s < nst; ++s) {
+    const int8_t* L = lds + (s % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < KK) {
+        read_frags(nxt, L, kk + 1);
+        mfmas(cur, 0, RN * RT);
+        // interleave the next step's 8 fragment reads with this step's MFMAs
+#pragma unroll
+        for (int q = 0; q < RN + RT; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, (RN * RT) / (RN + RT), 0);   // MFMAs
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        mfmas(cur, 0, RN * RT / 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < nst) {
+          // stage s+1 must have landed (later ones may stay in flight); this
+          // wave's fragment reads of stage s must be complete before the barrier
+          const int later = nst - 2 - s < STAGES - 2 ? nst - 2 - s : STAGES - 2;
+          wait_vm_lds(later);
+          bar();
+          if (s + STAGES < nst) issue(s % STAGES, (s + STAGES) * BK);
+          read_frags(nxt, lds + ((s + 1) % STAGES) * STAGE_BYTES, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(cur, RN * RT / 2, RN * RT - RN * RT / 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 
-  // epilogue: per block (i, j) and group g the lane holds outputs
-  // t = t0 + wt*WTT + j*32 + fr, n = n0 + wn*WTN + i*32 + 8g + 4*fc + 0..3
-  float sc[RT];
-  int tj[RT];
+  if (VEC) {
+    // ---- epilogue through LDS (requires N % (16 / output bytes) == 0, 16-byte aligned Y, ws)
+    __syncthreads();   // every wave is done with the operand ring
+    constexpr int OB = (OUT == kOutBF16) ? 2 : 4;
+    constexpr int ROWB = WTN * OB + 16;        // padded staging row
+    constexpr int CPRO = WTN * OB / 16;        // 16-byte chunks per output row
+    constexpr int RPI = 64 / CPRO;             // output rows per wave instruction
+    static_assert(NW * 32 * ROWB <= STAGES * STAGE_BYTES, "epilogue staging does not fit");
+    int8_t* E = lds + wave * (32 * ROWB);
+    float wsq[RN][4][4];
+    if (OUT != kOutI32) {
 #pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    tj[j] = t0 + wt * WTT + j * 32 + fr;
-    sc[j] = (OUT != kOutI32 && tj[j] < T) ? xs[tj[j]] : 0.0f;
-  }
+      for (int i = 0; i < RN; ++i)
 #pragma unroll
-  for (int i = 0; i < RN; ++i) {
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
+          const float4 w4 = (n < N) ? *reinterpret_cast<const float4*>(ws + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+          wsq[i][g][0] = w4.x; wsq[i][g][1] = w4.y; wsq[i][g][2] = w4.z; wsq[i][g][3] = w4.w;
+        }
+    }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
-      if (n >= N) continue;
-      float wsv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (OUT != kOutI32) {
-        if (VEC) {
-          const float4 w4 = *reinterpret_cast<const float4*>(ws + n);
-          wsv[0] = w4.x; wsv[1] = w4.y; wsv[2] = w4.z; wsv[3] = w4.w;
-        } else {
-          for (int e = 0; e < 4; ++e) wsv[e] = (n + e < N) ? ws[n + e] : 0.0f;
+    for (int j = 0; j < RT; ++j) {
+      const int t_l = t0 + wt * WTT + j * 32 + fr;
+      const float sc = (OUT != kOutI32 && t_l < T) ? xs[t_l] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < RN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          int8_t* dst = E + fr * ROWB + (i * 32 + 8 * g + 4 * fc) * OB;
+          if (OUT == kOutI32) {
+            *reinterpret_cast<v4i*>(dst) =
+                v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          } else {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (float)acc[i][j][4 * g + e] * (sc * wsq[i][g][e]);
+            if (OUT == kOutF32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              uint2 p;
+              p.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+              p.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+              *reinterpret_cast<uint2*>(dst) = p;
+            }
+          }
+        }
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + lane / CPRO, ch = lane % CPRO;
+        const v4i val = *reinterpret_cast<const v4i*>(E + row * ROWB + ch * 16);
+        const int t = t0 + wt * WTT + j * 32 + row;
+        const int n = n0 + wn * WTN + ch * (16 / OB);
+        if (t < T && n < N) *reinterpret_cast<v4i*>(static_cast<int8_t*>(Y) + ((int64_t)t * ldy + n) * OB) = val;
+      }
+    }
+  } else {
+    // ---- direct epilogue, element stores (any N, any alignment)
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const int t = t0 + wt * WTT + j * 32 + fr;
+      if (t >= T) continue;
+      const float sc = (OUT == kOutI32) ? 0.0f : xs[t];
+#pragma unroll
+      for (int i = 0; i < RN; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
+          if (n >= N) continue;
+          const int a4[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          float wsv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (OUT != kOutI32)
+            for (int e = 0; e < 4; ++e) wsv[e] = (n + e < N) ? ws[n + e] : 0.0f;
+          store4<OUT, false>(Y, (int64_t)t * ldy + n, N - n, a4, sc, wsv);
         }
       }
-#pragma unroll
-      for (int j = 0; j < RT; ++j) {
-        if (tj[j] >= T) continue;
-        const int a4[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
-        store4<OUT, VEC>(Y, (int64_t)tj[j] * ldy + n, N - n, a4, sc[j], wsv);
-      }
     }
   }
+#endif
 }
 
-template <int BN, int BT, int BK, int WN, int WT, bool VEC>
+template <int BN, int BT, int BK, int WN, int WT, int ST, bool VEC>
 static void launch_out(int out, dim3 grid, dim3 block, hipStream_t st, const int8_t* Xq, const float* xs,
                        const int8_t* Wq, const float* ws, int T, int N, int K, void* Y, int64_t ldy,
                        int tiles_n, int tiles_t) {
   switch (out) {
     case kOutF32:
-      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, kOutF32, VEC>), grid, block, 0, st, Xq, xs, Wq,
+      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, kOutF32, VEC>), grid, block, 0, st, Xq, xs, Wq,
                          ws, T, N, K, Y, ldy, tiles_n, tiles_t);
       break;
     case kOutBF16:
-      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, kOutBF16, VEC>), grid, block, 0, st, Xq, xs, Wq,
+      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, kOutBF16, VEC>), grid, block, 0, st, Xq, xs, Wq,
                          ws, T, N, K, Y, ldy, tiles_n, tiles_t);
       break;
     default:
-      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, kOutI32, VEC>), grid, block, 0, st, Xq, xs, Wq,
+      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, kOutI32, VEC>), grid, block, 0, st, Xq, xs, Wq,
                          ws, T, N, K, Y, ldy, tiles_n, tiles_t);
       break;
   }
 }
 
-template <int BN, int BT, int BK, int WN, int WT>
+template <int BN, int BT, int BK, int WN, int WT, int ST>
 static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
   // Split so that every operand slice handed to one launch spans < 2^31 bytes
   // (32-bit buffer offsets), counting one tile of overhang past the edge.
@@ -247,11 +374,13 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
       const float* ws = a.ws ? a.ws + nb : nullptr;
       void* Y = static_cast<char*>(a.Y) + (tb * a.N + nb) * osz;
       // a column slice of Y keeps 16-byte alignment only if nb is a multiple of 4
-      // a column slice of Y keeps 16-byte alignment only if nb is a multiple of 4
-      const bool vs = a.vec_store && nb % 4 == 0;
+      // the LDS-staged epilogue writes 16-byte row chunks: N must be a multiple of
+      // 16 / (output bytes) and the column slice must keep 16-byte alignment
+      const int per16 = a.out == kOutBF16 ? 8 : 4;
+      const bool vs = a.vec_store && a.N % per16 == 0 && nb % per16 == 0;
       const int K = (int)a.K;
-      if (vs) launch_out<BN, BT, BK, WN, WT, true>(a.out, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N, tiles_n, tiles_t);
-      else launch_out<BN, BT, BK, WN, WT, false>(a.out, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N, tiles_n, tiles_t);
+      if (vs) launch_out<BN, BT, BK, WN, WT, ST, true>(a.out, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N, tiles_n, tiles_t);
+      else launch_out<BN, BT, BK, WN, WT, ST, false>(a.out, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N, tiles_n, tiles_t);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -262,8 +391,8 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
 hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // 256x256 tiles when they fill the chip at least once, else 128x128.
   const int64_t big = ((a.N + 255) / 256) * ((a.T + 255) / 256);
-  if (big >= ncu) return gemm_cfg<256, 256, 64, 2, 2>(a, st);
-  return gemm_cfg<128, 128, 64, 2, 2>(a, st);
+  if (big >= ncu) return gemm_cfg<256, 256, 128, 2, 2, 2>(a, st);
+  return gemm_cfg<128, 128, 128, 2, 2, 2>(a, st);
 }
 
 // ---------------------------------------------------------------- generic path
