@@ -39,9 +39,42 @@ __device__ __forceinline__ int quant_code(float v, double rscale) {
   return (int)q;
 }
 
+// Code of the symmetric quantiser as the low byte of a binary32 bit pattern.
+// q = RN32(v / scale) is clamped to [-127, 127] (for integer bounds, clamping
+// before rounding gives the same integer as rounding first), then adding
+// 1.5 * 2^23 rounds it to an integer, ties to even, in the binary32 add itself;
+// the low byte of the sum's bit pattern is that integer in two's complement.
+__device__ __forceinline__ uint32_t quant_code_bits(float v, double rscale) {
+  float q = div_by_recip(v, rscale);
+  q = __builtin_fminf(__builtin_fmaxf(q, -(float)kQmax), (float)kQmax);
+  return __float_as_uint(q + 12582912.0f);
+}
+
+// Low bytes of four words -> one word (byte i from word i).
+__device__ __forceinline__ uint32_t pack4_lowbytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
          ((uint32_t)d << 24);
+}
+
+// Maximum over the 64 lanes of a non-negative value (so the integer order of the
+// bit patterns is the numeric order), by DPP lane exchanges: pairs, quads, half
+// rows, rows, then row 0 -> 1 and 2 -> 3, then row 1 -> 2..3; lane 63 ends with
+// the total, which is broadcast.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  int x = __float_as_int(v);
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));  // row_bcast15
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));  // row_bcast31
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

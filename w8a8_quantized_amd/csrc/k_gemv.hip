@@ -1,46 +1,78 @@
 // Decode-shaped W8A8 GEMM (few tokens, T <= 64) on gfx950.
 //
 // With a handful of tokens the layer is bound by streaming the int8 weights from
-// HBM (multigrid.ai "SmoothQuant Explained", section "Where it fits": at small
-// batch the multiply is not the bottleneck).  Every weight byte is used by all T
-// tokens at once, so there is no reuse to stage through LDS: each weight row
-// segment goes straight from HBM into MFMA operand registers.
-//
-// v_mfma_i32_16x16x64_i8 takes a 16-row block of Wq as operand A (rows = output
-// channels) and a 16-token block of Xq as operand B.  A lane supplies 16
-// consecutive bytes of one row; the 4 lane groups cover 64 consecutive bytes, so
-// one load instruction per operand reads 64 contiguous bytes of 16 rows.  Four
-// such MFMAs cover a 256-byte K block.  The 4 waves of a workgroup split K
-// (wave w takes blocks w, w+4, ...), and their int32 partial sums meet in LDS
-// (integer addition: exact, order-free).  The epilogue is the one of the prefill
-// kernel: y = fl32(fl32(acc) * fl32(x_scale[t] * w_scale[n])).
+// HBM (multigrid.ai "SmoothQuant Explained", section "Where it fits, and where it
+// does not": at small batch the multiply is not the bottleneck), so the kernel is
+// built around reading Wq at the highest rate the memory system gives:
+//   * each weight load instruction reads whole row segments (KC = 256 contiguous
+//     bytes of each of 4 rows), non-temporal, since every weight byte is used once;
+//   * loads run D chunks ahead in a register ring, so several chunks per wave are
+//     in flight;
+//   * each wave owns NB*16 output channels over all of K (no cross-wave reduction),
+//     and re-reads the small activation codes (L2-resident) once per chunk for all
+//     of them.
+// v_mfma_i32_16x16x64_i8 wants a 16-row block of Wq with lane l holding 16 bytes
+// of row l%16, so each chunk is transposed through a per-wave LDS tile: rows are
+// written as loaded and read back in the MFMA layout, with the 16-byte chunk
+// position XOR-swizzled by row so that the 16 rows of one read hit distinct banks.
+// The token codes are operand B (16 tokens per MFMA).  Integer accumulation is
+// exact; the epilogue is y = fl32(fl32(acc) * fl32(x_scale[t] * w_scale[n])).
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace sq {
 
-template <int NB, int TB, int OUT>
-__global__ __launch_bounds__(256) void gemv_i8_mfma_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
-    const float* __restrict__ ws, int64_t T, int64_t N, int64_t K, void* __restrict__ Y,
-    int vec_store) {
-  __shared__ v4i red[4][NB * TB][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, grp = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * (NB * 16);
+namespace {
 
-  const int8_t* wrow[NB];
-  const int8_t* xrow[TB];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+}  // namespace
+
+// Requires K % 16 == 0, N * K < 2^31 and T * K < 2^31 (the host splits larger N),
+// 16-byte aligned Xq and Wq.  One wave per workgroup; wave owns NB*16 channels.
+template <int NB, int TB, int OUT>
+__global__ __launch_bounds__(64) void gemv_i8_mfma_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
+    const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy, int vec_store) {
+  // The body exists only in the device pass (the host pass needs just the stub).
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KC = 256;                 // K bytes per chunk
+  constexpr int D = 2;                    // chunks in the register ring
+  constexpr int CPRW = KC / 16;           // 16-byte pieces per row per chunk (16)
+  constexpr int RPI = 64 / CPRW;          // rows per load instruction (4)
+  constexpr int NI = 16 * NB / RPI;       // weight loads per chunk per lane
+  constexpr int KS = KC / 64;             // MFMA k-steps per chunk (4)
+  constexpr int kOob = 0x7FFFFFF0;        // offset the range check turns into zeros
+  __shared__ __attribute__((aligned(1024))) int8_t lds[16 * NB * KC];
+  const int lane = threadIdx.x;
+  const int n0 = blockIdx.x * 16 * NB;
+  const __amdgpu_buffer_rsrc_t rsW = gemv_rsrc(Wq, N * K);   // rows >= N read as zeros
+  const __amdgpu_buffer_rsrc_t rsX = gemv_rsrc(Xq, T * K);   // tokens >= T read as zeros
+
+  // weight loads: instruction p covers rows p*RPI .. +RPI-1, lane -> (row, piece)
+  const int dr = lane / CPRW, dc = lane % CPRW;
+  int w_off[NI], w_lds[NI];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    int64_t n = n0 + i * 16 + r16; n = n < N ? n : N - 1;   // clamped rows are never stored
-    wrow[i] = Wq + n * K + grp * 16;
+  for (int p = 0; p < NI; ++p) {
+    const int rr = p * RPI + dr;
+    w_off[p] = (n0 + rr) * K + dc * 16;
+    w_lds[p] = rr * KC + ((dc ^ (rr & 15)) * 16);
   }
+  // operand reads: lane (fi = lane%16, fg = lane/16); k-step m uses piece m*4 + fg
+  const int fi = lane & 15, fg = lane >> 4;
+  int xoff[TB];
 #pragma unroll
-  for (int b = 0; b < TB; ++b) {
-    int64_t t = b * 16 + r16; t = t < T ? t : T - 1;
-    xrow[b] = Xq + t * K + grp * 16;
-  }
+  for (int b = 0; b < TB; ++b) xoff[b] = (b * 16 + fi) * K + fg * 16;
 
   v4i acc[NB][TB];
 #pragma unroll
@@ -48,97 +80,123 @@ __global__ __launch_bounds__(256) void gemv_i8_mfma_kernel(
 #pragma unroll
     for (int b = 0; b < TB; ++b) acc[i][b] = v4i{0, 0, 0, 0};
 
-  const int64_t nkb = (K + 255) / 256;
-
-  for (int64_t kb = wave; kb < nkb; kb += 4) {
-    const int64_t k = kb * 256;
-    v4i wv[NB][4], xv[TB][4];
+  v4i wr[D][NI], xv[D][TB][KS];
+  auto load = [&](auto slot_c, int k0) {
+    constexpr int sl = decltype(slot_c)::value;
+    const bool kin = dc * 16 < K - k0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t off = k + j * 64;
-      const bool ok = off + grp * 16 < K;
+    for (int p = 0; p < NI; ++p)   // cache policy 2: non-temporal
+      wr[sl][p] = __builtin_amdgcn_raw_buffer_load_b128(rsW, kin ? w_off[p] + k0 : kOob, 0, 2);
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        wv[i][j] = ok ? *reinterpret_cast<const v4i*>(wrow[i] + off) : v4i{0, 0, 0, 0};
+    for (int b = 0; b < TB; ++b)
 #pragma unroll
-      for (int b = 0; b < TB; ++b)
-        xv[b][j] = ok ? *reinterpret_cast<const v4i*>(xrow[b] + off) : v4i{0, 0, 0, 0};
-    }
+      for (int m = 0; m < KS; ++m)
+        xv[sl][b][m] = __builtin_amdgcn_raw_buffer_load_b128(
+            rsX, (k0 + m * 64 + fg * 16 < K) ? xoff[b] + k0 + m * 64 : kOob, 0, 0);
+  };
+  auto compute = [&](auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int p = 0; p < NI; ++p) *reinterpret_cast<v4i*>(lds + w_lds[p]) = wr[sl][p];
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+    for (int m = 0; m < KS; ++m) {
+      const int c = m * 4 + fg;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const v4i wv = *reinterpret_cast<const v4i*>(lds + (i * 16 + fi) * KC + ((c ^ fi) * 16));
 #pragma unroll
         for (int b = 0; b < TB; ++b)
-          acc[i][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[i][j], xv[b][j], acc[i][b], 0, 0, 0);
+          acc[i][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, xv[sl][b][m], acc[i][b], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nit = (K + KC - 1) / KC;
+  static_for(std::make_integer_sequence<int, D - 1>{}, [&](auto u) {
+    if (decltype(u)::value < nit) load(u, decltype(u)::value * KC);
+  });
+  for (int q0 = 0; q0 < nit; q0 += D) {
+    static_for(std::make_integer_sequence<int, D>{}, [&](auto u) {
+      constexpr int uu = decltype(u)::value;
+      const int q = q0 + uu;
+      if (q + D - 1 < nit) load(std::integral_constant<int, (uu + D - 1) % D>{}, (q + D - 1) * KC);
+      if (q < nit) compute(u);
+    });
   }
 
+  // epilogue: lane holds n = n0 + i*16 + 4*fg + 0..3 for token t = b*16 + fi
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int b = 0; b < TB; ++b) red[wave][i * TB + b][lane] = acc[i][b];
-  __syncthreads();
-
-  // wave w finishes blocks p = w, w+4, ...; lane holds n = n0 + i*16 + 4*grp + 0..3, t = b*16 + r16
-  for (int p = wave; p < NB * TB; p += 4) {
-    const int i = p / TB, b = p % TB;
-    const v4i s0 = red[0][p][lane], s1 = red[1][p][lane], s2 = red[2][p][lane], s3 = red[3][p][lane];
-    const int a4[4] = {s0[0] + s1[0] + s2[0] + s3[0], s0[1] + s1[1] + s2[1] + s3[1],
-                       s0[2] + s1[2] + s2[2] + s3[2], s0[3] + s1[3] + s2[3] + s3[3]};
-    const int64_t t = b * 16 + r16;
-    const int64_t n = n0 + i * 16 + 4 * grp;
-    if (t >= T || n >= N) continue;
-    const int64_t nrem = N - n;
-    const bool vec = vec_store && nrem >= 4;
-    if (OUT == kOutI32) {
-      int* y = static_cast<int*>(Y) + t * N + n;
-      if (vec) *reinterpret_cast<int4*>(y) = make_int4(a4[0], a4[1], a4[2], a4[3]);
-      else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = a4[e];
-      continue;
-    }
-    const float sc = xs[t];
-    float v[4];
-    for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (sc * ws[n + e]) : 0.0f;
-    if (OUT == kOutF32) {
-      float* y = static_cast<float*>(Y) + t * N + n;
-      if (vec) *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
-      else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = v[e];
-    } else {
-      uint16_t* y = static_cast<uint16_t*>(Y) + t * N + n;
-      if (vec) {
-        uint2 pk;
-        pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-        pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(y) = pk;
+    for (int b = 0; b < TB; ++b) {
+      const int t = b * 16 + fi, n = n0 + i * 16 + 4 * fg;
+      if (t >= T || n >= N) continue;
+      const int nrem = N - n;
+      const bool vec = vec_store && nrem >= 4;
+      const v4i a4 = acc[i][b];
+      if (OUT == kOutI32) {
+        int* y = static_cast<int*>(Y) + (int64_t)t * ldy + n;
+        if (vec) *reinterpret_cast<int4*>(y) = make_int4(a4[0], a4[1], a4[2], a4[3]);
+        else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = a4[e];
+        continue;
+      }
+      const float sc = xs[t];
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (sc * ws[n + e]) : 0.0f;
+      if (OUT == kOutF32) {
+        float* y = static_cast<float*>(Y) + (int64_t)t * ldy + n;
+        if (vec) *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
+        else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = v[e];
       } else {
-        for (int e = 0; e < 4 && e < nrem; ++e) y[e] = (uint16_t)f32_to_bf16(v[e]);
+        uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)t * ldy + n;
+        if (vec) {
+          uint2 pk;
+          pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+          pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(y) = pk;
+        } else {
+          for (int e = 0; e < 4 && e < nrem; ++e) y[e] = (uint16_t)f32_to_bf16(v[e]);
+        }
       }
     }
-  }
+#endif
 }
 
 template <int NB, int TB>
 static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
-  const int64_t G = (a.N + NB * 16 - 1) / (NB * 16);
-  dim3 grid((unsigned)G), block(256);
-  const int vs = a.vec_store ? 1 : 0;
-  switch (a.out) {
-    case kOutF32:
-      hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutF32>), grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y, vs);
-      break;
-    case kOutBF16:
-      hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutBF16>), grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y, vs);
-      break;
-    default:
-      hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutI32>), grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y, vs);
-      break;
+  // split N so that one launch's weight slice spans < 2^31 bytes (32-bit offsets)
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t n_chunk = ((lim / a.K - 16 * NB) / (16 * NB)) * (16 * NB);
+  const size_t osz = a.out == kOutBF16 ? 2 : 4;
+  for (int64_t nb = 0; nb < a.N; nb += n_chunk) {
+    const int N = (int)(a.N - nb < n_chunk ? a.N - nb : n_chunk);
+    dim3 grid((N + 16 * NB - 1) / (16 * NB)), block(64);
+    const int8_t* Wq = a.Wq + nb * a.K;
+    const float* ws = a.ws ? a.ws + nb : nullptr;
+    void* Y = static_cast<char*>(a.Y) + nb * osz;
+    const int vs = (a.vec_store && nb % 4 == 0) ? 1 : 0;
+    const int T = (int)a.T, K = (int)a.K;
+    switch (a.out) {
+      case kOutF32:
+        hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutF32>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs);
+        break;
+      case kOutBF16:
+        hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutBF16>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs);
+        break;
+      default:
+        hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutI32>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs);
+        break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   (void)ncu;
-  if (a.T <= 16) return gemv_cfg<2, 1>(a, st);
+  if (a.T <= 16) return gemv_cfg<4, 1>(a, st);
   if (a.T <= 32) return gemv_cfg<2, 2>(a, st);
   return gemv_cfg<2, 4>(a, st);
 }

@@ -61,7 +61,8 @@ __device__ __forceinline__ double recip64(double b) {
 }
 
 // MODE: 0 = activations (divide by s), 1 = weights (multiply by s).
-template <typename T, int MODE, bool HAS_S, int CPT>
+// FULL: K == CPT * 2048, every thread's chunks exist (no per-chunk masks).
+template <typename T, int MODE, bool HAS_S, int CPT, bool FULL>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A, int64_t R,
                                                          int64_t K, const float* __restrict__ s,
                                                          int8_t* __restrict__ Q,
@@ -79,37 +80,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float f = 1.0f;
-      if (HAS_S && c < nchunks) f = s[c * 8 + e];
+      if (HAS_S && (FULL || c < nchunks)) f = s[c * 8 + e];
       if (MODE == 0) rs[j][e] = HAS_S ? recip64((double)f) : 1.0;
       else sv[j][e] = f;
     }
   }
 
-  Raw8<T> cur[CPT], nxt[CPT];
-  int64_t r = blockIdx.x;
-  if (r < R) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int64_t c = (int64_t)j * 256 + tid;
-      if (c < nchunks) cur[j].load(A + r * K + c * 8); else cur[j].zero();
-    }
-  }
+  // one row: smoothed values, row maximum (wave DPP reduction + 4-entry LDS
+  // exchange), scale, codes
   int par = 0;
-  for (; r < R; r += gridDim.x) {
-    const int64_t rn = r + gridDim.x;
-    if (rn < R) {
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int64_t c = (int64_t)j * 256 + tid;
-        if (c < nchunks) nxt[j].load(A + rn * K + c * 8); else nxt[j].zero();
-      }
-    }
+  auto process = [&](const Raw8<T>* raw, int64_t r) {
     float v[CPT][8];
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       float x[8];
-      cur[j].unpack(x);
+      raw[j].unpack(x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float h = x[e];
@@ -118,7 +104,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
         m = fmaxf(m, fabsf(h));
       }
     }
-    m = wave_max(m);
+    m = wave_max_nonneg(m);
     if (lane == 0) red[par][wave] = m;
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
@@ -129,17 +115,38 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int64_t c = (int64_t)j * 256 + tid;
-      if (c < nchunks) {
+      if (FULL || c < nchunks) {
         uint2 o;
-        o.x = pack4_i8(quant_code(v[j][0], rsc), quant_code(v[j][1], rsc), quant_code(v[j][2], rsc),
-                       quant_code(v[j][3], rsc));
-        o.y = pack4_i8(quant_code(v[j][4], rsc), quant_code(v[j][5], rsc), quant_code(v[j][6], rsc),
-                       quant_code(v[j][7], rsc));
+        o.x = pack4_lowbytes(quant_code_bits(v[j][0], rsc), quant_code_bits(v[j][1], rsc),
+                             quant_code_bits(v[j][2], rsc), quant_code_bits(v[j][3], rsc));
+        o.y = pack4_lowbytes(quant_code_bits(v[j][4], rsc), quant_code_bits(v[j][5], rsc),
+                             quant_code_bits(v[j][6], rsc), quant_code_bits(v[j][7], rsc));
         *reinterpret_cast<uint2*>(Q + r * K + c * 8) = o;
       }
     }
+  };
+  auto load = [&](Raw8<T>* raw, int64_t r) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) cur[j] = nxt[j];
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t c = (int64_t)j * 256 + tid;
+      if (FULL || c < nchunks) raw[j].load(A + r * K + c * 8); else raw[j].zero();
+    }
+  };
+
+  // rows r, r + G, r + 2G, ... alternating between two register buffers; the
+  // next row's loads are in flight while the current one is processed
+  Raw8<T> ba[CPT], bb[CPT];
+  const int64_t G = gridDim.x;
+  int64_t r = blockIdx.x;
+  if (r < R) load(ba, r);
+  while (r < R) {
+    if (r + G < R) load(bb, r + G);
+    process(ba, r);
+    r += G;
+    if (r >= R) break;
+    if (r + G < R) load(ba, r + G);
+    process(bb, r);
+    r += G;
   }
 }
 
@@ -187,13 +194,18 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, i
   const int cpt = (int)((nchunks + 255) / 256);
   int64_t g = R < 3LL * ncu ? R : 3LL * ncu;
   dim3 grid((unsigned)g), block(256);
-  switch (cpt) {
-    case 1: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 1>), grid, block, 0, st, A, R, K, s, Q, scale); break;
-    case 2: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 2>), grid, block, 0, st, A, R, K, s, Q, scale); break;
-    case 3:
-    case 4: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 4>), grid, block, 0, st, A, R, K, s, Q, scale); break;
-    default: hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, 8>), grid, block, 0, st, A, R, K, s, Q, scale); break;
+  const int c2 = cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8;   // instantiated sizes
+  const bool full = K == (int64_t)c2 * 2048;
+#define SQ_QUANT_LAUNCH(C)                                                                              \
+  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true>), grid, block, 0, st, A, R, K, s, Q, scale); \
+  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false>), grid, block, 0, st, A, R, K, s, Q, scale);
+  switch (c2) {
+    case 1: SQ_QUANT_LAUNCH(1) break;
+    case 2: SQ_QUANT_LAUNCH(2) break;
+    case 4: SQ_QUANT_LAUNCH(4) break;
+    default: SQ_QUANT_LAUNCH(8) break;
   }
+#undef SQ_QUANT_LAUNCH
   return hipGetLastError();
 }
 
