@@ -5,8 +5,8 @@
 // output rows n of |W_nj|) is a pure HBM stream: each element is read once.
 // A workgroup is 4 waves; its 64 lanes each own one 16-byte column chunk and the
 // 4 waves walk interleaved rows of a row slab, so every wave load is 1 KB of one
-// row (fully coalesced).  The 4 partial maxima meet in LDS and one atomic max
-// per column and slab goes to the output.  |x| >= 0, so the unsigned order of
+// row (fully coalesced), with 8-16 rows per wave in flight.  The 4 partial
+// maxima meet in LDS and one atomic max per column and slab goes to the output.  |x| >= 0, so the unsigned order of
 // the binary32 bit patterns is the numeric order and an integer atomic max is
 // exact.
 #include "common.h"
@@ -17,6 +17,14 @@ namespace sq {
 __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void fill2_f32_kernel(float* __restrict__ p, float* __restrict__ q, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    p[i] = v;
+    q[i] = v;
+  }
 }
 
 // Element loaders: VEC elements of one row starting at column c.
@@ -45,8 +53,52 @@ template <> struct ChunkLoad<uint16_t, 1> {
   static __device__ __forceinline__ void abs(const uint16_t* p, float* o) { o[0] = fabsf(bf16_to_f32(*p)); }
 };
 
-// grid.x: groups of 64 chunks; grid.y: row slabs of `slab` rows.
-template <typename T, int VEC>
+// Running maximum of |x| over a chunk of VEC columns.  bf16 chunks keep four
+// packed pairs of 16-bit patterns with the sign bits cleared: for non-negative
+// bf16 values the unsigned order of the patterns is the numeric order, so one
+// packed unsigned max handles two columns.
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+template <typename T, int VEC> struct ColMax {
+  float m[VEC];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) m[i] = 0.0f;
+  }
+  __device__ __forceinline__ void add(const T* p) {
+    float a[VEC];
+    ChunkLoad<T, VEC>::abs(p, a);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) m[i] = fmaxf(m[i], a[i]);
+  }
+  __device__ __forceinline__ void result(float* o) const {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = m[i];
+  }
+};
+template <> struct ColMax<uint16_t, 8> {
+  uint32_t pm[4];
+  __device__ __forceinline__ void init() { pm[0] = pm[1] = pm[2] = pm[3] = 0u; }
+  __device__ __forceinline__ void add(const uint16_t* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      pm[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, pm[q]),
+                                                                     __builtin_bit_cast(us2, w[q])));
+  }
+  __device__ __forceinline__ void result(float* o) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = __uint_as_float(pm[q] << 16);
+      o[2 * q + 1] = __uint_as_float(pm[q] & 0xFFFF0000u);
+    }
+  }
+};
+
+// grid.x: groups of 64 chunks; grid.y: row slabs of `slab` rows.  Each wave
+// keeps U rows (of its 1 KB column strip) in flight.
+template <typename T, int VEC, int U>
 __global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A, int64_t rows,
                                                          int64_t cols, int64_t slab,
                                                          float* __restrict__ amax) {
@@ -56,29 +108,19 @@ __global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A
   const bool active = c0 < cols;   // cols % VEC == 0 on this path
   const int64_t r_begin = (int64_t)blockIdx.y * slab;
   const int64_t r_end = r_begin + slab < rows ? r_begin + slab : rows;
-  float m[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) m[i] = 0.0f;
+  ColMax<T, VEC> acc;
+  acc.init();
   if (active) {
     const T* p = A + c0;
     int64_t r = r_begin + wave;
-    // four rows in flight per wave
-    for (; r + 12 < r_end; r += 16) {
-      float a[4][VEC];
+    for (; r + 4 * (U - 1) < r_end; r += 4 * U) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ChunkLoad<T, VEC>::abs(p + (r + 4 * u) * cols, a[u]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) m[i] = fmaxf(m[i], a[u][i]);
+      for (int u = 0; u < U; ++u) acc.add(p + (r + 4 * u) * cols);
     }
-    for (; r < r_end; r += 4) {
-      float a[VEC];
-      ChunkLoad<T, VEC>::abs(p + r * cols, a);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) m[i] = fmaxf(m[i], a[i]);
-    }
+    for (; r < r_end; r += 4) acc.add(p + r * cols);
   }
+  float m[VEC];
+  acc.result(m);
 #pragma unroll
   for (int i = 0; i < VEC; ++i) part[wave][lane][i] = m[i];
   __syncthreads();
@@ -123,7 +165,12 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int VEC>
+hipError_t launch_fill2(float* p, float* q, int64_t n, float v, hipStream_t st) {
+  hipLaunchKernelGGL(fill2_f32_kernel, dim3(grid_1d(n, 256, 1024)), dim3(256), 0, st, p, q, n, v);
+  return hipGetLastError();
+}
+
+template <typename T, int VEC, int U>
 static hipError_t col_absmax_t(const T* A, int64_t rows, int64_t cols, float* amax, int ncu,
                                hipStream_t st) {
   const int64_t chunks = (cols + VEC - 1) / VEC;
@@ -136,7 +183,7 @@ static hipError_t col_absmax_t(const T* A, int64_t rows, int64_t cols, float* am
   if (slabs > 65535) slabs = 65535;
   int64_t slab = (rows + slabs - 1) / slabs;
   slabs = (rows + slab - 1) / slab;
-  hipLaunchKernelGGL((col_absmax_kernel<T, VEC>), dim3((unsigned)gx, (unsigned)slabs), dim3(256), 0,
+  hipLaunchKernelGGL((col_absmax_kernel<T, VEC, U>), dim3((unsigned)gx, (unsigned)slabs), dim3(256), 0,
                      st, A, rows, cols, slab, amax);
   return hipGetLastError();
 }
@@ -145,12 +192,12 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
                              bool vec_ok, int ncu, hipStream_t st) {
   if (bf16) {
     const uint16_t* a = static_cast<const uint16_t*>(A);
-    return vec_ok ? col_absmax_t<uint16_t, 8>(a, rows, cols, amax, ncu, st)
-                  : col_absmax_t<uint16_t, 1>(a, rows, cols, amax, ncu, st);
+    return vec_ok ? col_absmax_t<uint16_t, 8, 8>(a, rows, cols, amax, ncu, st)
+                  : col_absmax_t<uint16_t, 1, 4>(a, rows, cols, amax, ncu, st);
   }
   const float* a = static_cast<const float*>(A);
-  return vec_ok ? col_absmax_t<float, 4>(a, rows, cols, amax, ncu, st)
-                : col_absmax_t<float, 1>(a, rows, cols, amax, ncu, st);
+  return vec_ok ? col_absmax_t<float, 4, 16>(a, rows, cols, amax, ncu, st)
+                : col_absmax_t<float, 1, 4>(a, rows, cols, amax, ncu, st);
 }
 
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,

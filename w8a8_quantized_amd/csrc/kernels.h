@@ -13,6 +13,7 @@ constexpr int64_t kQuantFastMaxK = 16384;
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
 
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+hipError_t launch_fill2(float* p, float* q, int64_t n, float v, hipStream_t st);
 hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, float* amax,
                              bool vec_ok, int ncu, hipStream_t st);
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,

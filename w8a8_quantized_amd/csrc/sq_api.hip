@@ -110,9 +110,10 @@ sq_status sq_smooth_scales(const void* X, sq_dtype x_t, int64_t T, const void* W
   if (!in_dtype(x_t) || !in_dtype(w_t)) return SQ_ERR_DTYPE;
   if (T < 1 || N < 1 || K < 1) return SQ_ERR_SHAPE;
   if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
-  sq_status r = sq_col_absmax(X, x_t, T, K, x_absmax, 0, stream);
+  if (sq::launch_fill2(x_absmax, w_absmax, K, 0.0f, stream) != hipSuccess) return SQ_ERR_HIP;
+  sq_status r = sq_col_absmax(X, x_t, T, K, x_absmax, 1, stream);
   if (r != SQ_OK) return r;
-  r = sq_col_absmax(W, w_t, N, K, w_absmax, 0, stream);
+  r = sq_col_absmax(W, w_t, N, K, w_absmax, 1, stream);
   if (r != SQ_OK) return r;
   return sq_smooth_scales_from_absmax(x_absmax, w_absmax, K, alpha, s, stream);
 }
