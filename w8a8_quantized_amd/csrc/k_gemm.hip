@@ -258,8 +258,12 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     // ---- epilogue through LDS (requires N % (16 / output bytes) == 0, 16-byte aligned Y, ws)
     __syncthreads();   // every wave is done with the operand ring
     constexpr int OB = (OUT == kOutBF16) ? 2 : 4;
-    constexpr int ROWB = WTN * OB + 16;        // padded staging row
-    constexpr int CPRO = WTN * OB / 16;        // 16-byte chunks per output row
+    // Stage all RN column blocks of the wave tile at once when that fits in the
+    // operand ring, else one 32-column block at a time.
+    constexpr int EI = (NW * 32 * (WTN * OB + 16) <= STAGES * STAGE_BYTES) ? RN : 1;
+    constexpr int EW = EI * 32;                // outputs per staged row
+    constexpr int ROWB = EW * OB + 16;         // padded staging row
+    constexpr int CPRO = EW * OB / 16;         // 16-byte chunks per output row
     constexpr int RPI = 64 / CPRO;             // output rows per wave instruction
     static_assert(NW * 32 * ROWB <= STAGES * STAGE_BYTES, "epilogue staging does not fit");
     int8_t* E = lds + wave * (32 * ROWB);
@@ -279,34 +283,39 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
       const int t_l = t0 + wt * WTT + j * 32 + fr;
       const float sc = (OUT != kOutI32 && t_l < T) ? xs[t_l] : 0.0f;
 #pragma unroll
-      for (int i = 0; i < RN; ++i)
+      for (int ib = 0; ib < RN; ib += EI) {
+        // LDS accesses of one wave complete in order, so this round's writes
+        // follow the previous round's reads of the same staging rows.
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          int8_t* dst = E + fr * ROWB + (i * 32 + 8 * g + 4 * fc) * OB;
-          if (OUT == kOutI32) {
-            *reinterpret_cast<v4i*>(dst) =
-                v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          } else {
-            float v[4];
+        for (int i = ib; i < ib + EI; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (float)acc[i][j][4 * g + e] * (sc * wsq[i][g][e]);
-            if (OUT == kOutF32) {
-              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          for (int g = 0; g < 4; ++g) {
+            int8_t* dst = E + fr * ROWB + ((i - ib) * 32 + 8 * g + 4 * fc) * OB;
+            if (OUT == kOutI32) {
+              *reinterpret_cast<v4i*>(dst) =
+                  v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
             } else {
-              uint2 p;
-              p.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-              p.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-              *reinterpret_cast<uint2*>(dst) = p;
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = (float)acc[i][j][4 * g + e] * (sc * wsq[i][g][e]);
+              if (OUT == kOutF32) {
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+              } else {
+                uint2 p;
+                p.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+                p.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+                *reinterpret_cast<uint2*>(dst) = p;
+              }
             }
           }
-        }
 #pragma unroll
-      for (int it = 0; it < 32 / RPI; ++it) {
-        const int row = it * RPI + lane / CPRO, ch = lane % CPRO;
-        const v4i val = *reinterpret_cast<const v4i*>(E + row * ROWB + ch * 16);
-        const int t = t0 + wt * WTT + j * 32 + row;
-        const int n = n0 + wn * WTN + ch * (16 / OB);
-        if (t < T && n < N) *reinterpret_cast<v4i*>(static_cast<int8_t*>(Y) + ((int64_t)t * ldy + n) * OB) = val;
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int row = it * RPI + lane / CPRO, ch = lane % CPRO;
+          const v4i val = *reinterpret_cast<const v4i*>(E + row * ROWB + ch * 16);
+          const int t = t0 + wt * WTT + j * 32 + row;
+          const int n = n0 + wn * WTN + ib * 32 + ch * (16 / OB);
+          if (t < T && n < N) *reinterpret_cast<v4i*>(static_cast<int8_t*>(Y) + ((int64_t)t * ldy + n) * OB) = val;
+        }
       }
     }
   } else {
@@ -389,9 +398,11 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
-  // 256x256 tiles when they fill the chip at least once, else 128x128.
+  // 256x256 tiles when they fill the chip at least once, else 128x128.  The big
+  // tile runs 16 waves of 64x64 (4 per SIMD): with fewer, larger wave tiles the
+  // per-stage barrier and LDS latency are not covered (measured ~8% slower).
   const int64_t big = ((a.N + 255) / 256) * ((a.T + 255) / 256);
-  if (big >= ncu) return gemm_cfg<256, 256, 128, 2, 2, 2>(a, st);
+  if (big >= ncu) return gemm_cfg<256, 256, 128, 4, 4, 2>(a, st);
   return gemm_cfg<128, 128, 128, 2, 2, 2>(a, st);
 }
 
