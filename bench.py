@@ -48,6 +48,26 @@ def _quant_bytes(T, K, in_bytes):
     return in_bytes * T * K + 4 * K + T * K + 4 * T
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_pmc_heavy_t8192_and_decode_t16.md")
+
+
+def _gemm_traffic(workload):
+    """Memory-side bytes (read + written) of one GEMM launch from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary, or None when that summary is for
+    another workload or the GEMM source has changed since it was taken."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_SUMMARY).read().splitlines()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in lines if ": " in l and not l.startswith(("|", " ", "#")))
+    src = b"".join(open(os.path.join(ROOT, "w8a8_quantized_amd", "csrc", f), "rb").read()
+                   for f in ("k_gemm.hip", "common.h"))
+    if kv.get("workload") != workload or kv.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return float(kv["gemm_traffic_bytes_per_launch"])
+
+
 def _omp_threads():
     try:
         import ctypes
@@ -233,7 +253,8 @@ def main():
                    "step": "smooth_scales + quantize_weights + quant_act + w8a8_gemm"},
         "roofline": {"kernel": "gemm_i8_mfma (sq_w8a8_gemm)", "bound": "mfma",
                      "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                     "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": None,
+                     "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": _gemm_traffic(w.name),
+                     "traffic_unit": "bytes per launch (memory side, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "per_launch_ops": ops, "avg_launch_ms": t_gemm},
         "breakdown_ms_batched": {"smooth_scales": t_smooth, "quantize_weights": t_wq,
                                  "quant_act": t_quant, "w8a8_gemm": t_gemm_b},
