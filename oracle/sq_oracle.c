@@ -133,6 +133,49 @@ void sqo_quant_act(const float *X, int64_t T, int64_t K, const float *s,
     }
 }
 
+/* Per-tensor activation range.  [P2] "Where it fits, and where it does not":
+ * the O2 and O3 levels quantise the activations with one scale for the whole
+ * tensor, found from the values present (dynamic) or from calibration and then
+ * frozen (static); [P1] "Activations are a distribution, not a tensor" (static
+ * ranges come from calibration, dynamic ones cost a reduction over the tensor).
+ * amax = max over every t, k of |X_tk / s_k|: one IEEE division per element. */
+float sqo_act_tensor_absmax(const float *X, int64_t T, int64_t K, const float *s)
+{
+    float amax = 0.0f;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t k = 0; k < K; ++k) {
+            float v = s ? X[t * K + k] / s[k] : X[t * K + k];
+            float a = fabsf(v);
+            if (a > amax) amax = a;
+        }
+    return amax;
+}
+
+/* Per-tensor quantisation against a given range `clip`.  [P5] "The four
+ * operations", quantize_dequantize with its clip argument: scale = clip / n,
+ * code = clamp(round(v / scale), -n, n), so values beyond the range clamp to
+ * +-127; a zero range gives codes 0 and scale 1.  v = X_tk / s_k as for the
+ * per-token case.  Every token carries the same scale (x_scale[t] = scale for
+ * all t), so the per-token epilogue applies unchanged. */
+void sqo_quant_act_static(const float *X, int64_t T, int64_t K, const float *s, float clip,
+                          int8_t *Xq, float *x_scale)
+{
+    if (clip == 0.0f) {
+        for (int64_t t = 0; t < T; ++t) x_scale[t] = 1.0f;
+        memset(Xq, 0, (size_t)(T * K));
+        return;
+    }
+    float sc = clip / (float)SQO_N;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t k = 0; k < K; ++k) {
+            float v = s ? X[t * K + k] / s[k] : X[t * K + k];
+            Xq[t * K + k] = code_of(v, sc);
+        }
+        x_scale[t] = sc;
+    }
+}
+
 /* Integer matmul.  [P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk.
  * Accumulated in int64; returns 1 if any sum does not fit int32, else 0. */
 int sqo_int_gemm(const int8_t *Xq, const int8_t *Wq, int64_t T, int64_t N, int64_t K,

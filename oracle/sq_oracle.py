@@ -33,7 +33,8 @@ _lock = threading.Lock()
 __all__ = ["build", "col_absmax", "smooth_scales", "quantize_weights", "quant_act",
            "int_gemm", "int_gemm_at", "dequant", "dequant_at", "to_bf16", "w8a8_linear",
            "prepare", "w8a8_relative_error", "channel_max_over_median", "exact_product",
-           "widen_bf16", "set_threads"]
+           "widen_bf16", "set_threads", "act_tensor_absmax", "quant_act_static",
+           "quant_act_per_tensor"]
 
 GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
              "-std=c11", "-Wall"]
@@ -69,6 +70,10 @@ def _load():
             lib.sqo_dequant.argtypes = [P, P, P, I64, I64, P]
             lib.sqo_dequant_at.argtypes = [P, P, P, P, P, I64, P]
             lib.sqo_to_bf16.argtypes = [P, I64, P]
+            lib.sqo_act_tensor_absmax.argtypes = [P, I64, I64, P]
+            lib.sqo_act_tensor_absmax.restype = F
+            lib.sqo_quant_act_static.argtypes = [P, I64, I64, P, F, P, P]
+            lib.sqo_quant_act_static.restype = None
             for f in ("sqo_col_absmax", "sqo_smooth_scales", "sqo_quantize_weights",
                       "sqo_quant_act", "sqo_dequant", "sqo_dequant_at", "sqo_to_bf16"):
                 getattr(lib, f).restype = None
@@ -143,6 +148,40 @@ def quant_act(X, s=None):
     return Xq, xs
 
 
+def act_tensor_absmax(X, s=None) -> np.float32:
+    """[P2] section "Where it fits, and where it does not" (O2 / O3: one
+    activation scale per tensor); [P1] "Activations are a distribution": the
+    range of the smoothed tensor, max over all t, k of |X_tk / s_k|."""
+    X = _f32(X)
+    T, K = X.shape
+    s = None if s is None else _f32(s)
+    return np.float32(_load().sqo_act_tensor_absmax(_ptr(X), T, K, _ptr(s)))
+
+
+def quant_act_static(X, s, clip):
+    """[P5] "The four operations" with a given range (quantize_dequantize's
+    clip): scale = clip / 127, codes clamp(round(X_tk / s_k / scale)), values past
+    the range clamp to +-127; clip = 0 gives codes 0 and scale 1.  Returns
+    (Xq int8 [T,K], x_scale float32 [T], every entry the tensor's scale)."""
+    X = _f32(X)
+    T, K = X.shape
+    s = None if s is None else _f32(s)
+    clip = np.float32(clip)
+    assert np.isfinite(clip) and clip >= 0
+    Xq = np.empty((T, K), np.int8)
+    xs = np.empty(T, np.float32)
+    _load().sqo_quant_act_static(_ptr(X), T, K, _ptr(s), float(clip), _ptr(Xq), _ptr(xs))
+    return Xq, xs
+
+
+def quant_act_per_tensor(X, s=None):
+    """Dynamic per-tensor activation quantisation (O2): the static quantiser with
+    the tensor's own range.  Returns (Xq, x_scale [T], amax)."""
+    amax = act_tensor_absmax(X, s)
+    Xq, xs = quant_act_static(X, s, amax)
+    return Xq, xs, amax
+
+
 def int_gemm(Xq, Wq):
     """[P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk, exact int32."""
     Xq = np.ascontiguousarray(Xq, np.int8)
@@ -215,10 +254,16 @@ def prepare(X_stats, W, alpha):
     return dict(s=s, x_absmax=xa, w_absmax=wa, Wq=Wq, w_scale=ws)
 
 
-def w8a8_linear(X, s, Wq, w_scale):
-    """Runtime half: per-token quantisation of X diag(s)^-1, integer GEMM,
+def w8a8_linear(X, s, Wq, w_scale, act="token"):
+    """Runtime half: quantisation of X diag(s)^-1 (act="token": one scale per
+    token; act="tensor": one scale for the tensor, dynamic), integer GEMM,
     epilogue.  Returns (y float32 [T,N], Xq, x_scale, acc)."""
-    Xq, xs = quant_act(X, s)
+    if act == "token":
+        Xq, xs = quant_act(X, s)
+    elif act == "tensor":
+        Xq, xs, _ = quant_act_per_tensor(X, s)
+    else:
+        raise ValueError(act)
     acc = int_gemm(Xq, Wq)
     return dequant(acc, xs, w_scale), Xq, xs, acc
 
@@ -228,13 +273,14 @@ def exact_product(X, W):
     return np.asarray(X, np.float64) @ np.asarray(W, np.float64).T
 
 
-def w8a8_relative_error(X, W, alpha):
+def w8a8_relative_error(X, W, alpha, act="token"):
     """[P3] relative Frobenius error ||Y_q - Y|| / ||Y|| of the W8A8 layer with
-    per-token activations and per-output-channel weights; alpha=None: no
-    smoothing.  Statistics are taken from X itself, as in [P3]'s experiment."""
+    per-token (act="token") or per-tensor (act="tensor") activation scales and
+    per-output-channel weights; alpha=None: no smoothing.  Statistics are taken
+    from X itself, as in [P3]'s experiment."""
     X32, W32 = _f32(X), _f32(W)
     p = prepare(X32, W32, alpha)
-    y, *_ = w8a8_linear(X32, p["s"], p["Wq"], p["w_scale"])
+    y, *_ = w8a8_linear(X32, p["s"], p["Wq"], p["w_scale"], act=act)
     Y = exact_product(X, W)
     return float(np.linalg.norm(y.astype(np.float64) - Y) / np.linalg.norm(Y))
 

@@ -376,3 +376,98 @@ def test_oracle_threads_independent():
         O.set_threads(8)
     assert np.array_equal(y1, y2)
     assert math.isfinite(float(np.abs(y1).max()))
+
+
+# ------------------------------------------- per-tensor activation scales (O2 / O3)
+def test_page3_per_tensor_scales(page3):
+    """inferenceinterviews.com page, "A strong answer" (formats paragraph): with
+    per-tensor activation scales the same data gives 21% before, 2.9% after."""
+    X, W, _ = page3
+    g = {r[0]: float(r[1]) for r in read_golden("page3_per_tensor.txt")}
+    assert round(100 * O.w8a8_relative_error(X, W, None, act="tensor")) == g["error_before_percent"]
+    assert round(100 * O.w8a8_relative_error(X, W, 0.5, act="tensor"), 1) == \
+        g["error_after_alpha_0.5_percent"]
+
+
+def test_static_range_edge_127_6():
+    """maitreyasuin page, "The four operations": with a range fixed in advance a
+    value can land at 127.6 steps, which rounds to 128; clamped it is 127, never
+    the int8 wrap -128.  clip = 127 gives scale exactly 1."""
+    rules = {r[0]: r[1] for r in read_golden("quantizer_rules_p5.txt")}
+    edge = float(rules["edge_value"])
+    X = np.array([[edge, -edge, 128.4, 500.0, -1e4, 126.5, 0.5, -0.5, 1.5]], np.float32)
+    Xq, xs = O.quant_act_static(X, None, 127.0)
+    assert xs[0] == 1.0
+    assert Xq[0, 0] == int(rules["edge_clamped"]) and Xq[0, 1] == -int(rules["edge_clamped"])
+    assert Xq[0].tolist() == [127, -127, 127, 127, -127, 126, 0, 0, 2]
+    assert int(Xq.min()) >= -127
+
+
+def test_per_tensor_one_token_is_per_token():
+    """With one token the tensor is the token: per-tensor dynamic quantisation
+    must give exactly the per-token codes and scale (pinned separately)."""
+    rng = np.random.default_rng(21)
+    s = rng.uniform(0.2, 5, 777).astype(np.float32)
+    for _ in range(5):
+        x = (rng.standard_normal((1, 777)) * rng.uniform(0.1, 50)).astype(np.float32)
+        q1, s1 = O.quant_act(x, s)
+        q2, s2, amax = O.quant_act_per_tensor(x, s)
+        assert s1[0] == s2[0] and np.array_equal(q1, q2)
+        assert amax == np.max(np.abs(x[0] / s))
+
+
+def test_per_tensor_scale_is_largest_token_scale():
+    """amax over the tensor is the largest per-token amax, and fl32(a / 127) is
+    monotone in a, so the tensor scale equals the largest per-token scale; the
+    token that holds the maximum gets its per-token codes unchanged."""
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((40, 300)).astype(np.float32)
+    X[:, rng.choice(300, 3, replace=False)] *= 40
+    X[17] *= 3
+    s = rng.uniform(0.5, 2, 300).astype(np.float32)
+    qt, st = O.quant_act(X, s)
+    qT, sT, amax = O.quant_act_per_tensor(X, s)
+    assert np.all(sT == st.max())
+    t = int(np.argmax(st))
+    assert np.array_equal(qT[t], qt[t])
+    # every other token is on a coarser grid: its codes shrink in magnitude
+    assert np.all(np.abs(qT.astype(int)) <= np.abs(qt.astype(int)) + 1)
+
+
+def test_per_tensor_absmax_planted():
+    """The range is the largest |X_tk / s_k|: a planted value decides it."""
+    X = np.zeros((9, 33), np.float32)
+    X[3, 7] = -5.0
+    X[8, 30] = 9.0
+    s = np.ones(33, np.float32)
+    s[7] = 0.5        # -5 / 0.5 = -10 -> 10 wins over 9 / 1
+    assert O.act_tensor_absmax(X, s) == np.float32(10.0)
+    assert O.act_tensor_absmax(X, None) == np.float32(9.0)
+    assert O.act_tensor_absmax(np.zeros((2, 3), np.float32), None) == 0.0
+
+
+def test_static_range_clips_runtime_outliers():
+    """[P2] "Where it fits": the static level clips when a real input exceeds the
+    calibrated range.  Inside the range the round trip is within half a step;
+    beyond it the code is +-127 with the value's sign; a zero range gives codes 0
+    and scale 1 (maitreyasuin page, zero-range case)."""
+    rng = np.random.default_rng(23)
+    s = rng.uniform(0.5, 2, 256).astype(np.float32)
+    Xc = rng.standard_normal((64, 256)).astype(np.float32)
+    clip = O.act_tensor_absmax(Xc, s)
+    X = rng.standard_normal((64, 256)).astype(np.float32)
+    X[5, 10] = 4 * clip * s[10]
+    X[9, 11] = -6 * clip * s[11]
+    Xq, xs = O.quant_act_static(X, s, clip)
+    sc = np.float32(clip / np.float32(127))
+    assert np.all(xs == sc)
+    Xh = (X / s).astype(np.float32)
+    inside = np.abs(Xh) <= clip
+    assert not inside.all()
+    err = np.abs(Xq.astype(np.float64) * sc - Xh)
+    assert np.all(err[inside] <= 0.5 * sc * (1 + 1e-6))
+    assert np.all(Xq[~inside] == np.sign(Xh[~inside]) * 127)
+    assert Xq[5, 10] == 127 and Xq[9, 11] == -127
+    assert int(Xq.min()) >= -127 and int(Xq.max()) <= 127
+    q0, s0 = O.quant_act_static(X, s, 0.0)
+    assert np.all(s0 == 1.0) and not q0.any()
