@@ -68,6 +68,11 @@ def _gemm_traffic(workload):
     return float(kv["gemm_traffic_bytes_per_launch"])
 
 
+def _rate(nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"us": ms * 1e3, "bytes": nbytes, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+
+
 def _omp_threads():
     try:
         import ctypes
@@ -232,6 +237,14 @@ def main():
     t_wq = batched(lambda w_: sq.sq_quantize_weights(w_, s, Wq=Wq, w_scale=ws), Wc)
     t_quant = batched(lambda x_: sq.sq_quant_act(x_, s, Xq=Xq, x_scale=xs), Xc)
     t_gemm_b = batched(lambda _: sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=ydt, Y=Y), [None])
+    # per-tensor activation scales: the range reduction alone, the static-range
+    # quantiser (range from the first 512 tokens, as a calibration would give),
+    # and the dynamic per-tensor quantiser (reduction + quantiser)
+    amax_buf = torch.empty(1, device=dev)
+    clip_buf = sq.sq_act_absmax(X[:512], s)
+    t_tabs = batched(lambda x_: sq.sq_act_absmax(x_, s, amax=amax_buf), Xc)
+    t_qstat = batched(lambda x_: sq.sq_quant_act_static(x_, s, clip_buf, Xq=Xq, x_scale=xs), Xc)
+    t_qpt = batched(lambda x_: sq.sq_quant_act_per_tensor(x_, s, amax=amax_buf, Xq=Xq, x_scale=xs), Xc)
     del Wc, Xc
     ops = 2.0 * T * N * K
     ob = 2 if ydt == torch.bfloat16 else 4
@@ -261,6 +274,12 @@ def main():
         "linear_tops": ops / ((t_quant + t_gemm) * 1e-3) / 1e12,
         "quant_act": {"GB/s": qbytes / (t_quant * 1e-3) / 1e9,
                       "frac_hbm": qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": qbytes},
+        "per_tensor_act": {
+            "act_absmax": _rate(ib * T * K + 4 * K, t_tabs),
+            "quant_act_static": _rate(qbytes, t_qstat),
+            "quant_act_per_tensor": _rate(qbytes + ib * T * K + 4 * K, t_qpt),
+            "note": "bytes are algorithmic; the dynamic per-tensor quantiser reads X twice "
+                    "(range, then codes)"},
     }
     if not args.no_decode:
         del X, Xs, W, Wq, Xq, Y

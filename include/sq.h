@@ -12,7 +12,9 @@
  *     W diag(s) quantised with one scale per output channel;
  *   - at run time: X diag(s)^-1 quantised with one scale per token, computed
  *     from the values present (dynamic), then an int8 x int8 -> int32 GEMM whose
- *     epilogue multiplies by the token scale times the channel scale.
+ *     epilogue multiplies by the token scale times the channel scale;
+ *   - or, coarser, one activation scale for the whole tensor, from its own
+ *     range (dynamic) or from a calibrated range (static).
  *
  * Quantiser (maitreyasuin page, section "The four operations"): for one row v,
  * amax = max |v|; scale = amax / 127 (binary32 division); code =
@@ -142,6 +144,54 @@ sq_status sq_quantize_weights(const void *W, sq_dtype w_t, int64_t N, int64_t K,
  */
 sq_status sq_quant_act(const void *X, sq_dtype x_t, int64_t T, int64_t K,
                        const float *s, int8_t *Xq, float *x_scale, hipStream_t stream);
+
+/*
+ * Per-tensor activation range (multigrid.ai "SmoothQuant Explained", section
+ * "Where it fits, and where it does not": the O2 and O3 levels quantise the
+ * activations with one scale for the whole tensor, dynamic or static; katajob.com
+ * "Why are activations harder to quantize...", section "Activations are a
+ * distribution, not a tensor": static ranges are estimated during calibration
+ * and frozen):
+ *     amax[0] = max over all t, k of |X[t][k] / s[k]|      (binary32 quotients)
+ * With accumulate = 1 the result is max(amax[0], that value), so a calibration
+ * range can be gathered over several batches; with 0 the old value is ignored.
+ *   X        device, x_t = SQ_F32 or SQ_BF16, [T][K]
+ *   s        device float [K] (entries nonzero), or NULL for no smoothing
+ *   amax     device float [1], written (read as well when accumulate = 1)
+ */
+sq_status sq_act_absmax(const void *X, sq_dtype x_t, int64_t T, int64_t K,
+                        const float *s, float *amax, int accumulate, hipStream_t stream);
+
+/*
+ * Per-tensor activation quantisation against a given range, fused with the
+ * smoothing division (maitreyasuin page, "The four operations": quantize_dequantize
+ * with a clip; multigrid page, "Where it fits": the static level, which clips an
+ * input beyond the calibrated range):
+ *     X_hat[t][k] = X[t][k] / s[k]
+ *     scale = clip[0] / 127 (binary32), or 1.0 when clip[0] = 0
+ *     Xq[t][k] = clamp(round_half_even(X_hat[t][k] / scale), -127, 127)
+ *                (every code is 0 when clip[0] = 0)
+ *     x_scale[t] = scale for every t, so sq_w8a8_gemm applies unchanged
+ * Values beyond the range clamp to +-127.  X is read once; no reduction.
+ *   clip     device float [1]: a finite value >= 0 (for example a calibration
+ *            range from sq_act_absmax); it is read by the kernels, so another
+ *            value is outside the contract and is not diagnosed
+ *   X, s, Xq as for sq_quant_act;  x_scale  device float [T], written
+ */
+sq_status sq_quant_act_static(const void *X, sq_dtype x_t, int64_t T, int64_t K,
+                              const float *s, const float *clip, int8_t *Xq,
+                              float *x_scale, hipStream_t stream);
+
+/*
+ * Dynamic per-tensor activation quantisation (the O2 level): sq_act_absmax of X
+ * (accumulate = 0) into amax, then sq_quant_act_static with clip = amax.  X is
+ * read twice (the scale depends on the whole tensor before any code exists).
+ *   amax     device float [1], written with the tensor's range
+ *   X, s, Xq, x_scale as for sq_quant_act_static
+ */
+sq_status sq_quant_act_per_tensor(const void *X, sq_dtype x_t, int64_t T, int64_t K,
+                                  const float *s, float *amax, int8_t *Xq, float *x_scale,
+                                  hipStream_t stream);
 
 /*
  * W8A8 GEMM with int32 accumulation and the dequantising epilogue

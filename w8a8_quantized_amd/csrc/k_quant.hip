@@ -20,6 +20,13 @@
 // processed.  Both divisions of the method are done exactly as a multiply by a
 // binary64 reciprocal (see div_by_recip).
 //
+// Static-range mode (MODE 2, per-tensor activation scales): the range is given
+// (a calibrated clip, or the tensor's own range found by a reduction launched
+// before), so scale = clip / 127 is known up front and a row needs no reduction
+// and no barrier: read, divide, quantise, store (maitreyasuin page, "The four
+// operations", quantize_dequantize with its clip argument; clip = 0 gives scale 1
+// and codes 0).
+//
 // Slow path (any shape/alignment): one workgroup per row, two passes over the
 // row with plain IEEE binary32 divisions; identical results.
 #include "common.h"
@@ -60,19 +67,33 @@ __device__ __forceinline__ double recip64(double b) {
   return __builtin_fma(y, e, y);
 }
 
-// MODE: 0 = activations (divide by s), 1 = weights (multiply by s).
+// Static-range scale: clip / 127, or 1 (with a zero reciprocal, so that every
+// code is 0) when the range is 0.
+__device__ __forceinline__ void static_scale(const float* clip, float& scale, double& rscale) {
+  const float c = *clip;
+  scale = c == 0.0f ? 1.0f : c / (float)kQmax;
+  rscale = c == 0.0f ? 0.0 : 1.0 / (double)scale;
+}
+
+// MODE: 0 = activations, per-row range (divide by s); 1 = weights, per-row range
+// (multiply by s); 2 = activations, given range *clip (divide by s).
 // FULL: K == CPT * 2048, every thread's chunks exist (no per-chunk masks).
 template <typename T, int MODE, bool HAS_S, int CPT, bool FULL>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A, int64_t R,
                                                          int64_t K, const float* __restrict__ s,
+                                                         const float* __restrict__ clip,
                                                          int8_t* __restrict__ Q,
                                                          float* __restrict__ scale_out) {
   __shared__ float red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nchunks = K >> 3;
+  constexpr bool kDivide = MODE != 1;
+  float s_scale = 1.0f;
+  double s_rscale = 0.0;
+  if (MODE == 2) static_scale(clip, s_scale, s_rscale);
 
   // per-column factors for the chunks this thread owns
-  double rs[CPT][8];   // MODE 0: 1 / s
+  double rs[CPT][8];   // MODE 0, 2: 1 / s
   float sv[CPT][8];    // MODE 1: s
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
@@ -81,13 +102,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
     for (int e = 0; e < 8; ++e) {
       float f = 1.0f;
       if (HAS_S && (FULL || c < nchunks)) f = s[c * 8 + e];
-      if (MODE == 0) rs[j][e] = HAS_S ? recip64((double)f) : 1.0;
+      if (kDivide) rs[j][e] = HAS_S ? recip64((double)f) : 1.0;
       else sv[j][e] = f;
     }
   }
 
   // one row: smoothed values, row maximum (wave DPP reduction + 4-entry LDS
-  // exchange), scale, codes
+  // exchange) unless the range is given, scale, codes
   int par = 0;
   auto process = [&](const Raw8<T>* raw, int64_t r) {
     float v[CPT][8];
@@ -99,18 +120,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float h = x[e];
-        if (HAS_S) h = (MODE == 0) ? div_by_recip(x[e], rs[j][e]) : x[e] * sv[j][e];
+        if (HAS_S) h = kDivide ? div_by_recip(x[e], rs[j][e]) : x[e] * sv[j][e];
         v[j][e] = h;
         m = fmaxf(m, fabsf(h));
       }
     }
-    m = wave_max_nonneg(m);
-    if (lane == 0) red[par][wave] = m;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
-    par ^= 1;
-    const float scale = amax == 0.0f ? 1.0f : amax / (float)kQmax;
-    const double rsc = 1.0 / (double)scale;
+    float scale = s_scale;
+    double rsc = s_rscale;
+    if (MODE != 2) {
+      m = wave_max_nonneg(m);
+      if (lane == 0) red[par][wave] = m;
+      __syncthreads();
+      const float amax = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
+      par ^= 1;
+      scale = amax == 0.0f ? 1.0f : amax / (float)kQmax;
+      rsc = 1.0 / (double)scale;
+    }
     if (tid == 0) scale_out[r] = scale;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
@@ -158,29 +183,39 @@ template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) 
 template <typename T, int MODE>
 __global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restrict__ A, int64_t R,
                                                               int64_t K, const float* __restrict__ s,
+                                                              const float* __restrict__ clip,
                                                               int8_t* __restrict__ Q,
                                                               float* __restrict__ scale_out) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
+  const float c = MODE == 2 ? *clip : 0.0f;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const T* row = A + r * K;
-    float m = 0.0f;
-    for (int64_t k = tid; k < K; k += 256) {
-      float x = load1<T>(row + k);
-      if (s) x = (MODE == 0) ? x / s[k] : x * s[k];
-      m = fmaxf(m, fabsf(x));
+    float scale;
+    bool zero;
+    if (MODE == 2) {
+      zero = c == 0.0f;
+      scale = zero ? 1.0f : c / (float)kQmax;
+    } else {
+      float m = 0.0f;
+      for (int64_t k = tid; k < K; k += 256) {
+        float x = load1<T>(row + k);
+        if (s) x = (MODE == 1) ? x * s[k] : x / s[k];
+        m = fmaxf(m, fabsf(x));
+      }
+      m = wave_max(m);
+      if ((tid & 63) == 0) red[tid >> 6] = m;
+      __syncthreads();
+      const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      __syncthreads();
+      zero = amax == 0.0f;
+      scale = zero ? 1.0f : amax / (float)kQmax;
     }
-    m = wave_max(m);
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    const float scale = amax == 0.0f ? 1.0f : amax / (float)kQmax;
     if (tid == 0) scale_out[r] = scale;
     for (int64_t k = tid; k < K; k += 256) {
       float x = load1<T>(row + k);
-      if (s) x = (MODE == 0) ? x / s[k] : x * s[k];
-      float q = __builtin_rintf(x / scale);
+      if (s) x = (MODE == 1) ? x * s[k] : x / s[k];
+      float q = zero ? 0.0f : __builtin_rintf(x / scale);
       q = fminf(fmaxf(q, -(float)kQmax), (float)kQmax);
       Q[r * K + k] = (int8_t)(int)q;
     }
@@ -188,8 +223,8 @@ __global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restric
 }
 
 template <typename T, int MODE, bool HAS_S>
-static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, int8_t* Q,
-                             float* scale, int ncu, hipStream_t st) {
+static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, const float* clip,
+                             int8_t* Q, float* scale, int ncu, hipStream_t st) {
   const int64_t nchunks = K / 8;
   const int cpt = (int)((nchunks + 255) / 256);
   int64_t g = R < 3LL * ncu ? R : 3LL * ncu;
@@ -197,8 +232,8 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, i
   const int c2 = cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8;   // instantiated sizes
   const bool full = K == (int64_t)c2 * 2048;
 #define SQ_QUANT_LAUNCH(C)                                                                              \
-  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true>), grid, block, 0, st, A, R, K, s, Q, scale); \
-  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false>), grid, block, 0, st, A, R, K, s, Q, scale);
+  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true>), grid, block, 0, st, A, R, K, s, clip, Q, scale); \
+  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false>), grid, block, 0, st, A, R, K, s, clip, Q, scale);
   switch (c2) {
     case 1: SQ_QUANT_LAUNCH(1) break;
     case 2: SQ_QUANT_LAUNCH(2) break;
@@ -210,29 +245,34 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, i
 }
 
 template <typename T, int MODE>
-static hipError_t quant_dispatch(const T* A, int64_t R, int64_t K, const float* s, int8_t* Q,
-                                 float* scale, bool vec_ok, int ncu, hipStream_t st) {
+static hipError_t quant_dispatch(const T* A, int64_t R, int64_t K, const float* s, const float* clip,
+                                 int8_t* Q, float* scale, bool vec_ok, int ncu, hipStream_t st) {
   if (vec_ok && K <= kQuantFastMaxK) {
-    return s ? quant_fast<T, MODE, true>(A, R, K, s, Q, scale, ncu, st)
-             : quant_fast<T, MODE, false>(A, R, K, s, Q, scale, ncu, st);
+    return s ? quant_fast<T, MODE, true>(A, R, K, s, clip, Q, scale, ncu, st)
+             : quant_fast<T, MODE, false>(A, R, K, s, clip, Q, scale, ncu, st);
   }
   int64_t g = R < 8LL * ncu ? R : 8LL * ncu;
   hipLaunchKernelGGL((quant_rows_slow_kernel<T, MODE>), dim3((unsigned)g), dim3(256), 0, st, A, R, K,
-                     s, Q, scale);
+                     s, clip, Q, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_rows(const void* A, bool bf16, bool weights, int64_t R, int64_t K,
-                             const float* s, int8_t* Q, float* scale, bool vec_ok, int ncu,
+template <typename T>
+static hipError_t quant_mode(const T* A, int mode, int64_t R, int64_t K, const float* s,
+                             const float* clip, int8_t* Q, float* scale, bool vec_ok, int ncu,
                              hipStream_t st) {
-  if (bf16) {
-    const uint16_t* a = static_cast<const uint16_t*>(A);
-    return weights ? quant_dispatch<uint16_t, 1>(a, R, K, s, Q, scale, vec_ok, ncu, st)
-                   : quant_dispatch<uint16_t, 0>(a, R, K, s, Q, scale, vec_ok, ncu, st);
+  switch (mode) {
+    case kQuantWeights: return quant_dispatch<T, 1>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    case kQuantActStatic: return quant_dispatch<T, 2>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    default: return quant_dispatch<T, 0>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
   }
-  const float* a = static_cast<const float*>(A);
-  return weights ? quant_dispatch<float, 1>(a, R, K, s, Q, scale, vec_ok, ncu, st)
-                 : quant_dispatch<float, 0>(a, R, K, s, Q, scale, vec_ok, ncu, st);
+}
+
+hipError_t launch_quant_rows(const void* A, bool bf16, int mode, int64_t R, int64_t K,
+                             const float* s, const float* clip, int8_t* Q, float* scale,
+                             bool vec_ok, int ncu, hipStream_t st) {
+  if (bf16) return quant_mode(static_cast<const uint16_t*>(A), mode, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+  return quant_mode(static_cast<const float*>(A), mode, R, K, s, clip, Q, scale, vec_ok, ncu, st);
 }
 
 }  // namespace sq

@@ -134,6 +134,112 @@ __global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A
   }
 }
 
+// Range of the whole smoothed activation tensor, max over t, k of
+// |fl32(A_tk / s_k)| (the per-tensor activation levels of multigrid.ai
+// "SmoothQuant Explained", section "Where it fits, and where it does not").
+// Rounded division by |s_k| is monotone in |A_tk|, and rounding to nearest is
+// symmetric, so each column's largest quotient is fl32(max_t |A_tk| / |s_k|):
+// the workgroup takes the column maxima of |A| over its row slab exactly as
+// col_absmax_kernel does, divides once per column, reduces to one value and
+// issues a single atomic max (instead of one per column).
+template <typename T, int VEC, int U, bool HAS_S>
+__global__ __launch_bounds__(256) void tensor_absmax_kernel(const T* __restrict__ A, int64_t rows,
+                                                            int64_t cols, int64_t slab,
+                                                            const float* __restrict__ s,
+                                                            float* __restrict__ amax) {
+  __shared__ float part[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * VEC;
+  const bool active = c0 < cols;   // cols % VEC == 0 on this path
+  const int64_t r_begin = (int64_t)blockIdx.y * slab;
+  const int64_t r_end = r_begin + slab < rows ? r_begin + slab : rows;
+  ColMax<T, VEC> acc;
+  acc.init();
+  if (active) {
+    const T* p = A + c0;
+    int64_t r = r_begin + wave;
+    for (; r + 4 * (U - 1) < r_end; r += 4 * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc.add(p + (r + 4 * u) * cols);
+    }
+    for (; r < r_end; r += 4) acc.add(p + r * cols);
+  }
+  float m[VEC];
+  acc.result(m);
+  float v = 0.0f;
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v = fmaxf(v, HAS_S ? m[i] / fabsf(s[c0 + i]) : m[i]);
+  }
+  v = wave_max_nonneg(v);
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(reinterpret_cast<unsigned int*>(amax),
+              __float_as_uint(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]))));
+}
+
+// Same range, row-walking form for rows of at most 16384 elements that are
+// 16-byte aligned multiples of 8: a workgroup owns whole rows (thread t holds
+// the 8-element chunks t, t + 256, ...), walks row groups r0 = U * blockIdx.x,
+// + U * gridDim.x, ... and issues the loads of U complete rows before folding
+// them into per-column running maxima of |A| (packed for bf16).  Every HBM read
+// is a contiguous row; the last group reuses row R-1 in place of rows past the
+// end (harmless for a maximum) and chunks past the row end re-read its last
+// chunk, so the loads carry no conditions.
+template <typename T, bool HAS_S, int CPT, int U, bool FULL>
+__global__ __launch_bounds__(256) void tensor_absmax_rows_kernel(const T* __restrict__ A, int64_t R,
+                                                                 int64_t K,
+                                                                 const float* __restrict__ s,
+                                                                 float* __restrict__ amax) {
+  __shared__ float part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nchunks = K >> 3;
+  constexpr int VEC = 16 / sizeof(T) < 8 ? 16 / sizeof(T) : 8;   // elements per 16-byte load
+  constexpr int LPC = 8 / VEC;                                     // loads per 8-element chunk
+  ColMax<T, VEC> acc[CPT][LPC];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int h = 0; h < LPC; ++h) acc[j][h].init();
+  for (int64_t r0 = (int64_t)blockIdx.x * U; r0 < R; r0 += (int64_t)gridDim.x * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + u < R ? r0 + u : R - 1;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        // chunks past the row end re-read the last chunk; their maxima are
+        // ignored below
+        int64_t c = (int64_t)j * 256 + tid;
+        if (!FULL && c >= nchunks) c = nchunks - 1;
+#pragma unroll
+        for (int h = 0; h < LPC; ++h) acc[j][h].add(A + r * K + c * 8 + h * VEC);
+      }
+    }
+  }
+  float v = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int64_t c = (int64_t)j * 256 + tid;
+    if (FULL || c < nchunks) {
+#pragma unroll
+      for (int h = 0; h < LPC; ++h) {
+        float m[VEC];
+        acc[j][h].result(m);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+          v = fmaxf(v, HAS_S ? m[i] / fabsf(s[c * 8 + h * VEC + i]) : m[i]);
+      }
+    }
+  }
+  v = wave_max_nonneg(v);
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (tid == 0)
+    atomicMax(reinterpret_cast<unsigned int*>(amax),
+              __float_as_uint(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]))));
+}
+
 // s_j = max(xa_j, 1e-8)^alpha / max(wa_j, 1e-8)^(1 - alpha), binary64, rounded once
 // (multigrid.ai "SmoothQuant Explained", section "Alpha: how much difficulty to
 // move"; 1e-8 floor from the maitreyasuin page, section "Route it, or move it").
@@ -198,6 +304,70 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
   const float* a = static_cast<const float*>(A);
   return vec_ok ? col_absmax_t<float, 4, 16>(a, rows, cols, amax, ncu, st)
                 : col_absmax_t<float, 1, 4>(a, rows, cols, amax, ncu, st);
+}
+
+template <typename T, int VEC, int U>
+static hipError_t tensor_absmax_t(const T* A, int64_t rows, int64_t cols, const float* s, float* amax,
+                                  int ncu, hipStream_t st) {
+  const int64_t chunks = (cols + VEC - 1) / VEC;
+  const int64_t gx = (chunks + 63) / 64;
+  int64_t slabs = 8LL * ncu / gx;
+  if (slabs < 1) slabs = 1;
+  const int64_t max_slabs = (rows + 15) / 16;
+  if (slabs > max_slabs) slabs = max_slabs;
+  if (slabs > 65535) slabs = 65535;
+  int64_t slab = (rows + slabs - 1) / slabs;
+  slabs = (rows + slab - 1) / slab;
+  const dim3 grid((unsigned)gx, (unsigned)slabs), block(256);
+  if (s) hipLaunchKernelGGL((tensor_absmax_kernel<T, VEC, U, true>), grid, block, 0, st, A, rows, cols, slab, s, amax);
+  else hipLaunchKernelGGL((tensor_absmax_kernel<T, VEC, U, false>), grid, block, 0, st, A, rows, cols, slab, s, amax);
+  return hipGetLastError();
+}
+
+// Row-walking range kernel: rows of K = 8 * 256 * CPT' elements (CPT' <= CPT).
+// U rows in flight per group (about 16 / 32 loads of 16 bytes per thread for
+// bf16 / fp32); one workgroup per CU for bf16, two for fp32 (measured best on
+// 8192 x 8192: 24.6 us bf16, 48 us fp32, against 35 / 64 us for the slab form).
+template <typename T, bool HAS_S, int CPT>
+static hipError_t tensor_absmax_rows_t(const T* A, int64_t R, int64_t K, const float* s, float* amax,
+                                       int ncu, hipStream_t st) {
+  constexpr int U0 = (sizeof(T) == 2 ? 16 : 32) / CPT;
+  constexpr int U = U0 > 16 ? 16 : U0;
+  int64_t g = (R + U - 1) / U;
+  const int64_t cap = (sizeof(T) == 2 ? 1 : 2) * (int64_t)ncu;
+  if (g > cap) g = cap;
+  if (K == (int64_t)CPT * 2048)
+    hipLaunchKernelGGL((tensor_absmax_rows_kernel<T, HAS_S, CPT, U, true>), dim3((unsigned)g), dim3(256), 0, st, A, R, K, s, amax);
+  else
+    hipLaunchKernelGGL((tensor_absmax_rows_kernel<T, HAS_S, CPT, U, false>), dim3((unsigned)g), dim3(256), 0, st, A, R, K, s, amax);
+  return hipGetLastError();
+}
+
+template <typename T, bool HAS_S>
+static hipError_t tensor_absmax_rows(const T* A, int64_t R, int64_t K, const float* s, float* amax,
+                                     int ncu, hipStream_t st) {
+  const int64_t cpt = (K / 8 + 255) / 256;
+  if (cpt <= 1) return tensor_absmax_rows_t<T, HAS_S, 1>(A, R, K, s, amax, ncu, st);
+  if (cpt <= 2) return tensor_absmax_rows_t<T, HAS_S, 2>(A, R, K, s, amax, ncu, st);
+  if (cpt <= 4) return tensor_absmax_rows_t<T, HAS_S, 4>(A, R, K, s, amax, ncu, st);
+  return tensor_absmax_rows_t<T, HAS_S, 8>(A, R, K, s, amax, ncu, st);
+}
+
+template <typename T>
+static hipError_t tensor_absmax_any(const T* A, int64_t rows, int64_t cols, const float* s, float* amax,
+                                    bool vec_ok, int ncu, hipStream_t st) {
+  constexpr int VEC = 16 / sizeof(T);
+  if (vec_ok && cols % 8 == 0 && cols <= 16384)
+    return s ? tensor_absmax_rows<T, true>(A, rows, cols, s, amax, ncu, st)
+             : tensor_absmax_rows<T, false>(A, rows, cols, s, amax, ncu, st);
+  if (vec_ok) return tensor_absmax_t<T, VEC, (VEC == 8 ? 8 : 16)>(A, rows, cols, s, amax, ncu, st);
+  return tensor_absmax_t<T, 1, 4>(A, rows, cols, s, amax, ncu, st);
+}
+
+hipError_t launch_tensor_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, const float* s,
+                                float* amax, bool vec_ok, int ncu, hipStream_t st) {
+  if (bf16) return tensor_absmax_any(static_cast<const uint16_t*>(A), rows, cols, s, amax, vec_ok, ncu, st);
+  return tensor_absmax_any(static_cast<const float*>(A), rows, cols, s, amax, vec_ok, ncu, st);
 }
 
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,

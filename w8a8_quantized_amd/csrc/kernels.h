@@ -18,9 +18,16 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
                              bool vec_ok, int ncu, hipStream_t st);
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
                                 hipStream_t st);
-hipError_t launch_quant_rows(const void* A, bool bf16, bool weights, int64_t R, int64_t K,
-                             const float* s, int8_t* Q, float* scale, bool vec_ok, int ncu,
-                             hipStream_t st);
+// Row quantiser modes: per-token activations (divide by s, per-row range),
+// per-output-channel weights (multiply by s, per-row range), activations against
+// the range *clip (divide by s, one scale for every row).
+enum QuantMode { kQuantAct = 0, kQuantWeights = 1, kQuantActStatic = 2 };
+hipError_t launch_quant_rows(const void* A, bool bf16, int mode, int64_t R, int64_t K,
+                             const float* s, const float* clip, int8_t* Q, float* scale,
+                             bool vec_ok, int ncu, hipStream_t st);
+// amax[0] = max(amax[0], max over the tensor of |A_tk / s_k|)  (s may be NULL).
+hipError_t launch_tensor_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, const float* s,
+                                float* amax, bool vec_ok, int ncu, hipStream_t st);
 
 struct GemmArgs {
   const int8_t* Xq;

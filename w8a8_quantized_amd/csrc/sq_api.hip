@@ -62,8 +62,29 @@ sq_status run_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const fl
 sq_status run_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
                         int8_t* Xq, float* xs, hipStream_t st) {
   const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
-  return hip_status(
-      sq::launch_quant_rows(X, x_t == SQ_BF16, false, T, K, s, Xq, xs, vec, cu_count(), st));
+  return hip_status(sq::launch_quant_rows(X, x_t == SQ_BF16, sq::kQuantAct, T, K, s, nullptr, Xq, xs,
+                                          vec, cu_count(), st));
+}
+
+sq_status check_act_args(const void* X, sq_dtype x_t, int64_t T, int64_t K) {
+  if (!X) return SQ_ERR_NULL;
+  if (!in_dtype(x_t)) return SQ_ERR_DTYPE;
+  if (T < 1 || K < 1) return SQ_ERR_SHAPE;
+  return SQ_OK;
+}
+
+sq_status run_act_absmax(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
+                         float* amax, int accumulate, hipStream_t st) {
+  if (!accumulate && sq::launch_fill(amax, 1, 0.0f, st) != hipSuccess) return SQ_ERR_HIP;
+  const bool vec = rows_vec16(X, K, esize(x_t));
+  return hip_status(sq::launch_tensor_absmax(X, x_t == SQ_BF16, T, K, s, amax, vec, cu_count(), st));
+}
+
+sq_status run_quant_static(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
+                           const float* clip, int8_t* Xq, float* xs, hipStream_t st) {
+  const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
+  return hip_status(sq::launch_quant_rows(X, x_t == SQ_BF16, sq::kQuantActStatic, T, K, s, clip, Xq,
+                                          xs, vec, cu_count(), st));
 }
 
 }  // namespace
@@ -124,8 +145,8 @@ sq_status sq_quantize_weights(const void* W, sq_dtype w_t, int64_t N, int64_t K,
   if (!in_dtype(w_t)) return SQ_ERR_DTYPE;
   if (N < 1 || K < 1) return SQ_ERR_SHAPE;
   const bool vec = (K % 8 == 0) && rows_vec16(W, K, esize(w_t)) && aligned16(Wq);
-  return hip_status(
-      sq::launch_quant_rows(W, w_t == SQ_BF16, true, N, K, s, Wq, w_scale, vec, cu_count(), stream));
+  return hip_status(sq::launch_quant_rows(W, w_t == SQ_BF16, sq::kQuantWeights, N, K, s, nullptr, Wq,
+                                          w_scale, vec, cu_count(), stream));
 }
 
 sq_status sq_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s, int8_t* Xq,
@@ -134,6 +155,32 @@ sq_status sq_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, const 
   if (!in_dtype(x_t)) return SQ_ERR_DTYPE;
   if (T < 1 || K < 1) return SQ_ERR_SHAPE;
   return run_quant_act(X, x_t, T, K, s, Xq, x_scale, stream);
+}
+
+sq_status sq_act_absmax(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
+                        float* amax, int accumulate, hipStream_t stream) {
+  sq_status r = check_act_args(X, x_t, T, K);
+  if (r != SQ_OK) return r;
+  if (!amax) return SQ_ERR_NULL;
+  return run_act_absmax(X, x_t, T, K, s, amax, accumulate, stream);
+}
+
+sq_status sq_quant_act_static(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
+                              const float* clip, int8_t* Xq, float* x_scale, hipStream_t stream) {
+  sq_status r = check_act_args(X, x_t, T, K);
+  if (r != SQ_OK) return r;
+  if (!clip || !Xq || !x_scale) return SQ_ERR_NULL;
+  return run_quant_static(X, x_t, T, K, s, clip, Xq, x_scale, stream);
+}
+
+sq_status sq_quant_act_per_tensor(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s,
+                                  float* amax, int8_t* Xq, float* x_scale, hipStream_t stream) {
+  sq_status r = check_act_args(X, x_t, T, K);
+  if (r != SQ_OK) return r;
+  if (!amax || !Xq || !x_scale) return SQ_ERR_NULL;
+  r = run_act_absmax(X, x_t, T, K, s, amax, 0, stream);
+  if (r != SQ_OK) return r;
+  return run_quant_static(X, x_t, T, K, s, amax, Xq, x_scale, stream);
 }
 
 sq_status sq_w8a8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,

@@ -34,6 +34,9 @@ _SIGS = {
     "sq_smooth_scales": ([_P, _I, _I64, _P, _I, _I64, _I64, _F, _P, _P, _P, _P], _I),
     "sq_quantize_weights": ([_P, _I, _I64, _I64, _P, _P, _P, _P], _I),
     "sq_quant_act": ([_P, _I, _I64, _I64, _P, _P, _P, _P], _I),
+    "sq_act_absmax": ([_P, _I, _I64, _I64, _P, _P, _I, _P], _I),
+    "sq_quant_act_static": ([_P, _I, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "sq_quant_act_per_tensor": ([_P, _I, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "sq_w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_linear_workspace_size": ([_I64, _I64], _SZ),
     "sq_w8a8_linear": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
@@ -141,6 +144,45 @@ def sq_quant_act(X, s=None, Xq=None, x_scale=None):
     _check(_lib.sq_quant_act(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(Xq), _ptr(x_scale),
                              _stream(X.device)))
     return Xq, x_scale
+
+
+def sq_act_absmax(X, s=None, amax=None, accumulate=False):
+    """Range of X diag(s)^-1 over the whole tensor, as a device float [1]."""
+    T, K = X.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    amax = _want(amax, (1,), torch.float32, X.device)
+    _check(_lib.sq_act_absmax(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(amax), int(bool(accumulate)),
+                              _stream(X.device)))
+    return amax
+
+
+def sq_quant_act_static(X, s, clip, Xq=None, x_scale=None):
+    """Per-tensor int8 codes of X diag(s)^-1 against the range clip (device float
+    [1]).  Returns (Xq, x_scale), every x_scale entry the tensor's scale."""
+    T, K = X.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    if clip is None or clip.numel() != 1 or clip.dtype != torch.float32:
+        raise ValueError("clip must be a float32 tensor of one element")
+    Xq = _want(Xq, (T, K), torch.int8, X.device)
+    x_scale = _want(x_scale, (T,), torch.float32, X.device)
+    _check(_lib.sq_quant_act_static(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(clip), _ptr(Xq),
+                                    _ptr(x_scale), _stream(X.device)))
+    return Xq, x_scale
+
+
+def sq_quant_act_per_tensor(X, s=None, amax=None, Xq=None, x_scale=None):
+    """Dynamic per-tensor int8 codes of X diag(s)^-1.  Returns (Xq, x_scale, amax)."""
+    T, K = X.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    amax = _want(amax, (1,), torch.float32, X.device)
+    Xq = _want(Xq, (T, K), torch.int8, X.device)
+    x_scale = _want(x_scale, (T,), torch.float32, X.device)
+    _check(_lib.sq_quant_act_per_tensor(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(amax), _ptr(Xq),
+                                        _ptr(x_scale), _stream(X.device)))
+    return Xq, x_scale, amax
 
 
 def sq_w8a8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
