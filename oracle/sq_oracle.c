@@ -176,6 +176,69 @@ void sqo_quant_act_static(const float *X, int64_t T, int64_t K, const float *s, 
     }
 }
 
+/* Folding the smoothing division into the preceding normalisation.  [P2] "Why
+ * the rescaling is free at runtime": divide the norm's per-channel weight vector
+ * elementwise by s, so the norm emits already-smoothed activations; [P3] "A
+ * strong answer": 1/s_j folds into the preceding RMSNorm gain.  A LayerNorm's
+ * bias is divided the same way (it is added after the gain, so it must carry the
+ * same 1/s).  out[k] = in[k] / s[k], one IEEE division. */
+void sqo_fold_gain(const float *in, const float *s, int64_t K, float *out)
+{
+    for (int64_t k = 0; k < K; ++k) out[k] = in[k] / s[k];
+}
+
+/* Per-token statistics of the normalisation that precedes the linear layer.
+ * The pages name RMSNorm and LayerNorm but do not write them out; the textbook
+ * definitions are used:
+ *   RMSNorm   rstd_t = 1 / sqrt(mean_k x_tk^2 + eps)                (mean_t = 0)
+ *   LayerNorm mean_t = mean_k x_tk,  rstd_t = 1 / sqrt(mean_k (x_tk - mean_t)^2 + eps)
+ * Sums and the square root in binary64 (two passes for the variance), each
+ * statistic rounded once to binary32. */
+void sqo_norm_stats(const float *X, int64_t T, int64_t K, int layer, float eps,
+                    float *mean, float *rstd)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *x = X + t * K;
+        double mu = 0.0;
+        if (layer) {
+            for (int64_t k = 0; k < K; ++k) mu += (double)x[k];
+            mu /= (double)K;
+        }
+        double v = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double d = (double)x[k] - mu;
+            v += d * d;
+        }
+        v /= (double)K;
+        mean[t] = (float)mu;
+        rstd[t] = (float)(1.0 / sqrt(v + (double)eps));
+    }
+}
+
+/* Normalised, gained activations in binary32, one rounding per operation, in
+ * the order the definitions read (centre, scale by rstd, multiply by the gain,
+ * add the bias):
+ *   RMSNorm   h = (x * rstd) * gain
+ *   LayerNorm h = ((x - mean) * rstd) * gain + bias      (bias may be NULL)
+ * With the smoothing folded into gain and bias, h is the smoothed activation
+ * that the per-token quantiser takes. */
+void sqo_norm_apply(const float *X, int64_t T, int64_t K, int layer, const float *mean,
+                    const float *rstd, const float *gain, const float *bias, float *H)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t k = 0; k < K; ++k) {
+            float x = X[t * K + k];
+            float c = layer ? x - mean[t] : x;
+            float n = c * rstd[t];
+            float h = n * gain[k];
+            if (layer && bias) h = h + bias[k];
+            H[t * K + k] = h;
+        }
+    }
+}
+
 /* Integer matmul.  [P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk.
  * Accumulated in int64; returns 1 if any sum does not fit int32, else 0. */
 int sqo_int_gemm(const int8_t *Xq, const int8_t *Wq, int64_t T, int64_t N, int64_t K,

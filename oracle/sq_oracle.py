@@ -34,7 +34,7 @@ __all__ = ["build", "col_absmax", "smooth_scales", "quantize_weights", "quant_ac
            "int_gemm", "int_gemm_at", "dequant", "dequant_at", "to_bf16", "w8a8_linear",
            "prepare", "w8a8_relative_error", "channel_max_over_median", "exact_product",
            "widen_bf16", "set_threads", "act_tensor_absmax", "quant_act_static",
-           "quant_act_per_tensor"]
+           "quant_act_per_tensor", "fold_gain", "norm_stats", "norm_apply", "norm_quant_act"]
 
 GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
              "-std=c11", "-Wall"]
@@ -74,6 +74,11 @@ def _load():
             lib.sqo_act_tensor_absmax.restype = F
             lib.sqo_quant_act_static.argtypes = [P, I64, I64, P, F, P, P]
             lib.sqo_quant_act_static.restype = None
+            lib.sqo_fold_gain.argtypes = [P, P, I64, P]
+            lib.sqo_norm_stats.argtypes = [P, I64, I64, ctypes.c_int, F, P, P]
+            lib.sqo_norm_apply.argtypes = [P, I64, I64, ctypes.c_int, P, P, P, P, P]
+            for f in ("sqo_fold_gain", "sqo_norm_stats", "sqo_norm_apply"):
+                getattr(lib, f).restype = None
             for f in ("sqo_col_absmax", "sqo_smooth_scales", "sqo_quantize_weights",
                       "sqo_quant_act", "sqo_dequant", "sqo_dequant_at", "sqo_to_bf16"):
                 getattr(lib, f).restype = None
@@ -180,6 +185,55 @@ def quant_act_per_tensor(X, s=None):
     amax = act_tensor_absmax(X, s)
     Xq, xs = quant_act_static(X, s, amax)
     return Xq, xs, amax
+
+
+NORM_KINDS = {"rms": 0, "layer": 1}
+
+
+def fold_gain(v, s):
+    """[P2] "Why the rescaling is free at runtime"; [P3] "A strong answer": fold
+    diag(s)^-1 into the preceding norm's gain (or bias): v / s per channel."""
+    v, s = _f32(v), _f32(s)
+    assert v.shape == s.shape and v.ndim == 1
+    out = np.empty_like(v)
+    _load().sqo_fold_gain(_ptr(v), _ptr(s), v.size, _ptr(out))
+    return out
+
+
+def norm_stats(X, kind, eps):
+    """Per-token (mean, rstd) of the textbook RMSNorm / LayerNorm (binary64 sums,
+    rounded once); mean is 0 for RMSNorm."""
+    X = _f32(X)
+    T, K = X.shape
+    mean = np.empty(T, np.float32)
+    rstd = np.empty(T, np.float32)
+    _load().sqo_norm_stats(_ptr(X), T, K, NORM_KINDS[kind], float(np.float32(eps)), _ptr(mean),
+                           _ptr(rstd))
+    return mean, rstd
+
+
+def norm_apply(X, kind, mean, rstd, gain, bias=None):
+    """h = ((x - mean) * rstd) * gain (+ bias), binary32, one rounding per op."""
+    X = _f32(X)
+    T, K = X.shape
+    mean, rstd, gain = _f32(mean), _f32(rstd), _f32(gain)
+    assert mean.size == T and rstd.size == T and gain.size == K
+    bias = None if bias is None else _f32(bias)
+    H = np.empty((T, K), np.float32)
+    _load().sqo_norm_apply(_ptr(X), T, K, NORM_KINDS[kind], _ptr(mean), _ptr(rstd), _ptr(gain),
+                           _ptr(bias), _ptr(H))
+    return H
+
+
+def norm_quant_act(X, kind, gain, bias=None, eps=1e-6, stats=None):
+    """The producer in front of the layer: normalisation with the smoothing
+    folded into its gain (and bias), then dynamic per-token int8 of the result.
+    `stats` = (mean, rstd) replaces the oracle's own statistics (to compare codes
+    given the same binary32 statistics).  Returns (Xq, x_scale, mean, rstd)."""
+    mean, rstd = norm_stats(X, kind, eps) if stats is None else (_f32(stats[0]), _f32(stats[1]))
+    H = norm_apply(X, kind, mean, rstd, gain, bias)
+    Xq, xs = quant_act(H, None)
+    return Xq, xs, mean, rstd
 
 
 def int_gemm(Xq, Wq):

@@ -471,3 +471,90 @@ def test_static_range_clips_runtime_outliers():
     assert int(Xq.min()) >= -127 and int(Xq.max()) <= 127
     q0, s0 = O.quant_act_static(X, s, 0.0)
     assert np.all(s0 == 1.0) and not q0.any()
+
+
+# ------------------------------------ normalisation with the smoothing folded in
+def _norm_case(seed, T=24, K=320):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    X[:, rng.choice(K, 4, replace=False)] *= 30
+    X += np.float32(0.3) * rng.standard_normal((T, 1)).astype(np.float32)   # row offsets
+    g = (1 + 0.2 * rng.standard_normal(K)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(K)).astype(np.float32)
+    return X, g, b
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1e-2, 4.0])
+def test_norms_match_library_float64(eps):
+    """The textbook RMSNorm and LayerNorm (torch.nn.functional, float64) against
+    the oracle's binary32 chain: every element within its few roundings."""
+    import torch
+    X, g, b = _norm_case(31)
+    x64 = torch.from_numpy(X.astype(np.float64))
+    K = X.shape[1]
+    ref = torch.nn.functional.rms_norm(x64, (K,), torch.from_numpy(g.astype(np.float64)), eps).numpy()
+    mean, rstd = O.norm_stats(X, "rms", eps)
+    assert np.all(mean == 0)
+    H = O.norm_apply(X, "rms", mean, rstd, g)
+    assert np.all(np.abs(H - ref) <= 1e-6 * np.abs(ref) + 1e-30)
+    ref = torch.nn.functional.layer_norm(x64, (K,), torch.from_numpy(g.astype(np.float64)),
+                                         torch.from_numpy(b.astype(np.float64)), eps).numpy()
+    mean, rstd = O.norm_stats(X, "layer", eps)
+    H = O.norm_apply(X, "layer", mean, rstd, g, b)
+    tol = 1e-6 * (np.abs(ref) + np.abs(g)[None, :] * (np.abs(mean) * rstd)[:, None] + np.abs(b)[None, :])
+    assert np.all(np.abs(H - ref) <= tol)
+
+
+def test_norm_fold_equals_unfused_pipeline():
+    """[P2] "Why the rescaling is free at runtime": normalising with gain g / s
+    gives the same smoothed activations as normalising with g and then dividing
+    by s, up to one rounding; the codes agree except for rare neighbours."""
+    X, g, b = _norm_case(32, T=64, K=512)
+    rng = np.random.default_rng(33)
+    s = rng.uniform(0.2, 6.0, X.shape[1]).astype(np.float32)
+    for kind, bias in (("rms", None), ("layer", b)):
+        gf = O.fold_gain(g, s)
+        bf = None if bias is None else O.fold_gain(bias, s)
+        Xq, xs, mean, rstd = O.norm_quant_act(X, kind, gf, bf, eps=1e-6)
+        H = O.norm_apply(X, kind, mean, rstd, g, bias)     # unfused: norm, then divide
+        Xq2, xs2 = O.quant_act(H, s)
+        np.testing.assert_allclose(xs, xs2, rtol=1e-6)
+        d = np.abs(Xq.astype(int) - Xq2.astype(int))
+        assert d.max() <= 1 and (d > 0).mean() < 1e-3, kind
+
+
+def test_norm_zero_and_constant_rows():
+    """A zero row normalises to zero (codes 0, scale 1, rstd = 1/sqrt(eps)); a
+    constant row has zero variance, so LayerNorm returns the bias itself."""
+    K = 64
+    X = np.zeros((3, K), np.float32)
+    X[1] = 2.5
+    X[2] = np.linspace(-1, 1, K, dtype=np.float32)
+    g = np.full(K, 1.5, np.float32)
+    b = np.linspace(-3, 1, K, dtype=np.float32)
+    Xq, xs, mean, rstd = O.norm_quant_act(X, "rms", g, eps=0.25)
+    assert rstd[0] == 2.0 and xs[0] == 1.0 and not Xq[0].any()
+    mean, rstd = O.norm_stats(X, "layer", 0.25)
+    assert mean[1] == 2.5 and rstd[1] == 2.0
+    H = O.norm_apply(X, "layer", mean, rstd, g, b)
+    assert np.array_equal(H[1], b)
+    Xq, xs, _, _ = O.norm_quant_act(X, "layer", g, b, eps=0.25)
+    qb, sb = O.quant_act(b[None, :], None)
+    assert np.array_equal(Xq[1], qb[0]) and xs[1] == sb[0]
+
+
+def test_rms_scale_invariance():
+    """With eps = 0, scaling a token by 4 scales mean(x^2) by 16 and rstd by 1/4
+    exactly, so the codes and scales are unchanged."""
+    X, g, _ = _norm_case(34)
+    a = O.norm_quant_act(X, "rms", g, eps=0.0)
+    c = O.norm_quant_act(X * np.float32(4), "rms", g, eps=0.0)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+    assert np.array_equal(c[3] * np.float32(4), a[3])
+
+
+def test_fold_gain_is_division():
+    rng = np.random.default_rng(35)
+    g = rng.uniform(-2, 2, 1000).astype(np.float32)
+    s = rng.uniform(0.01, 50, 1000).astype(np.float32)
+    assert np.array_equal(O.fold_gain(g, s), (g / s).astype(np.float32))
