@@ -245,6 +245,13 @@ def main():
     t_tabs = batched(lambda x_: sq.sq_act_absmax(x_, s, amax=amax_buf), Xc)
     t_qstat = batched(lambda x_: sq.sq_quant_act_static(x_, s, clip_buf, Xq=Xq, x_scale=xs), Xc)
     t_qpt = batched(lambda x_: sq.sq_quant_act_per_tensor(x_, s, amax=amax_buf, Xq=Xq, x_scale=xs), Xc)
+    # the producer in front of the layer: RMSNorm (gain folded with s) + per-token int8
+    gen = torch.Generator(device=dev).manual_seed(7)
+    gain = 1.0 + 0.2 * torch.randn(K, device=dev, generator=gen)
+    gfold = sq.sq_fold_norm_gain(gain, s)
+    m_buf, r_buf = torch.empty(T, device=dev), torch.empty(T, device=dev)
+    t_norm = batched(lambda x_: sq.sq_norm_quant_act(x_, "rms", gfold, Xq=Xq, x_scale=xs, mean=m_buf,
+                                                     rstd=r_buf), Xc)
     del Wc, Xc
     ops = 2.0 * T * N * K
     ob = 2 if ydt == torch.bfloat16 else 4
@@ -280,6 +287,7 @@ def main():
             "quant_act_per_tensor": _rate(qbytes + ib * T * K + 4 * K, t_qpt),
             "note": "bytes are algorithmic; the dynamic per-tensor quantiser reads X twice "
                     "(range, then codes)"},
+        "norm_quant_act_rms": _rate(ib * T * K + 4 * K + T * K + 4 * T + 8 * T, t_norm),
     }
     if not args.no_decode:
         del X, Xs, W, Wq, Xq, Y

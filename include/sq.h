@@ -57,7 +57,8 @@ typedef enum sq_status {
     SQ_ERR_ALPHA = 3,      /* alpha is NaN or outside [0, 1]                     */
     SQ_ERR_DTYPE = 4,      /* dtype not accepted for that argument               */
     SQ_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required            */
-    SQ_ERR_HIP = 6         /* the HIP runtime rejected a launch                  */
+    SQ_ERR_HIP = 6,        /* the HIP runtime rejected a launch                  */
+    SQ_ERR_ARG = 7         /* an argument value is not accepted (see the call)   */
 } sq_status;
 
 typedef enum sq_dtype {
@@ -192,6 +193,52 @@ sq_status sq_quant_act_static(const void *X, sq_dtype x_t, int64_t T, int64_t K,
 sq_status sq_quant_act_per_tensor(const void *X, sq_dtype x_t, int64_t T, int64_t K,
                                   const float *s, float *amax, int8_t *Xq, float *x_scale,
                                   hipStream_t stream);
+
+/* Normalisation in front of the layer. */
+typedef enum sq_norm {
+    SQ_NORM_RMS = 0,       /* RMSNorm: no centring, no bias  */
+    SQ_NORM_LAYER = 1      /* LayerNorm: centring, optional bias */
+} sq_norm;
+
+/*
+ * Fold the smoothing division into the preceding normalisation's per-channel
+ * vector (multigrid.ai "SmoothQuant Explained", section "Why the rescaling is
+ * free at runtime": divide the norm's weight vector elementwise by s; a
+ * LayerNorm bias is folded the same way):  out[k] = v[k] / s[k]  (binary32).
+ *   v, s     device float [K];  out  device float [K], written (may alias v)
+ */
+sq_status sq_fold_norm_gain(const float *v, const float *s, int64_t K, float *out,
+                            hipStream_t stream);
+
+/*
+ * Normalisation fused with per-token int8 quantisation: the producer of a
+ * smoothed W8A8 layer's input (multigrid page, "Why the rescaling is free at
+ * runtime": with diag(s)^-1 folded into its gain the norm emits smoothed
+ * activations; inferenceinterviews page, "A strong answer": 1/s_j folds into the
+ * preceding RMSNorm gain).  The pages name the norms without writing them out;
+ * the textbook forms are used, per token t:
+ *   RMSNorm    rstd_t = 1 / sqrt(mean_k X[t][k]^2 + eps),  mean_t = 0
+ *              h[t][k] = (X[t][k] * rstd_t) * gain[k]
+ *   LayerNorm  mean_t = mean_k X[t][k],
+ *              rstd_t = 1 / sqrt(mean_k (X[t][k] - mean_t)^2 + eps)
+ *              h[t][k] = ((X[t][k] - mean_t) * rstd_t) * gain[k] + bias[k]
+ * The statistics are summed in binary64 and rounded once to binary32; h is
+ * binary32, one rounding per operation in the order written.  Then h is
+ * quantised exactly as sq_quant_act quantises X_hat (x_scale[t] = max_k |h| / 127,
+ * scale 1 and codes 0 for a zero row).  X is read once; h is never stored.
+ *   X          device, x_t = SQ_F32 or SQ_BF16, [T][K] (the norm's input)
+ *   kind       SQ_NORM_RMS or SQ_NORM_LAYER
+ *   gain       device float [K]: the norm's gain with 1/s folded in
+ *              (sq_fold_norm_gain), or the plain gain for an unsmoothed layer
+ *   bias       device float [K] or NULL (LayerNorm only, folded the same way)
+ *   eps        finite, >= 0
+ *   Xq         device int8 [T][K], written;  x_scale  device float [T], written
+ *   mean, rstd device float [T] each, or NULL; written with the statistics
+ * SQ_ERR_ARG: unknown kind, a bias with SQ_NORM_RMS, or eps negative / not finite.
+ */
+sq_status sq_norm_quant_act(const void *X, sq_dtype x_t, int64_t T, int64_t K, sq_norm kind,
+                            const float *gain, const float *bias, float eps, int8_t *Xq,
+                            float *x_scale, float *mean, float *rstd, hipStream_t stream);
 
 /*
  * W8A8 GEMM with int32 accumulation and the dequantising epilogue

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "w8a8_quantized_amd", "libsq.so")
 HEADER = os.path.join(ROOT, "include", "sq.h")
 
-SQ_OK, SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALPHA, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP = range(7)
+(SQ_OK, SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALPHA, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP,
+ SQ_ERR_ARG) = range(8)
 F32, BF16, I32 = 0, 1, 2
 
 
@@ -39,6 +40,11 @@ def lib():
     L.sq_w8a8_linear_workspace_size.argtypes = [I64, I64]
     L.sq_w8a8_linear_workspace_size.restype = ctypes.c_size_t
     L.sq_w8a8_linear.argtypes = [P, I, P, P, P, I64, I64, I64, P, I, P, ctypes.c_size_t, P]
+    L.sq_act_absmax.argtypes = [P, I, I64, I64, P, P, I, P]
+    L.sq_quant_act_static.argtypes = [P, I, I64, I64, P, P, P, P, P]
+    L.sq_quant_act_per_tensor.argtypes = [P, I, I64, I64, P, P, P, P, P]
+    L.sq_fold_norm_gain.argtypes = [P, P, I64, P, P]
+    L.sq_norm_quant_act.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P, P]
     return L
 
 
@@ -61,7 +67,7 @@ def test_binding_names_match_header():
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         s = lib.sq_status_string(code).decode()
         assert s.startswith("SQ_"), s
     assert b"unknown" in lib.sq_status_string(99)
@@ -123,3 +129,34 @@ def test_workspace(lib):
     # workspace must be 256-byte aligned
     assert lib.sq_w8a8_linear(FAKE, F32, None, FAKE, FAKE, 16, 4, 64, FAKE, F32,
                               ctypes.c_void_p(0x1010), need, None) == SQ_ERR_WORKSPACE
+
+
+def test_per_tensor_arguments(lib):
+    assert lib.sq_act_absmax(FAKE, F32, 4, 4, None, None, 0, None) == SQ_ERR_NULL
+    assert lib.sq_act_absmax(None, F32, 4, 4, None, FAKE, 0, None) == SQ_ERR_NULL
+    assert lib.sq_act_absmax(FAKE, F32, 0, 4, None, FAKE, 0, None) == SQ_ERR_SHAPE
+    assert lib.sq_act_absmax(FAKE, I32, 4, 4, None, FAKE, 0, None) == SQ_ERR_DTYPE
+    assert lib.sq_quant_act_static(FAKE, F32, 4, 4, None, None, FAKE, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_quant_act_static(FAKE, BF16, 4, -2, None, FAKE, FAKE, FAKE, None) == SQ_ERR_SHAPE
+    # the dynamic call validates everything before its first launch
+    assert lib.sq_quant_act_per_tensor(FAKE, F32, 4, 4, None, FAKE, None, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_quant_act_per_tensor(FAKE, F32, 4, 4, None, FAKE, FAKE, None, None) == SQ_ERR_NULL
+
+
+def test_norm_arguments(lib):
+    assert lib.sq_fold_norm_gain(FAKE, None, 4, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_fold_norm_gain(FAKE, FAKE, 0, FAKE, None) == SQ_ERR_SHAPE
+    ok = dict(X=FAKE, t=BF16, T=4, K=16, kind=0, g=FAKE, b=None, eps=1e-6, q=FAKE, xs=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.sq_norm_quant_act(a["X"], a["t"], a["T"], a["K"], a["kind"], a["g"], a["b"],
+                                     a["eps"], a["q"], a["xs"], None, None, None)
+    assert call(g=None) == SQ_ERR_NULL
+    assert call(q=None) == SQ_ERR_NULL
+    assert call(T=0) == SQ_ERR_SHAPE
+    assert call(t=I32) == SQ_ERR_DTYPE
+    assert call(kind=2) == SQ_ERR_ARG
+    assert call(kind=0, b=FAKE) == SQ_ERR_ARG          # RMSNorm has no bias
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert call(eps=eps) == SQ_ERR_ARG

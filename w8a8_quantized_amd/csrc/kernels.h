@@ -29,6 +29,14 @@ hipError_t launch_quant_rows(const void* A, bool bf16, int mode, int64_t R, int6
 hipError_t launch_tensor_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, const float* s,
                                 float* amax, bool vec_ok, int ncu, hipStream_t st);
 
+// Normalisation (RMSNorm, or LayerNorm when `layer`) with folded gain / bias,
+// then per-token int8 of the result; mean / rstd may be NULL.
+hipError_t launch_norm_quant(const void* A, bool bf16, bool layer, int64_t R, int64_t K, const float* gain,
+                             const float* bias, float eps, int8_t* Q, float* scale, float* mean, float* rstd,
+                             bool vec_ok, int ncu, hipStream_t st);
+// out[k] = v[k] / s[k]
+hipError_t launch_fold_gain(const float* v, const float* s, int64_t K, float* out, hipStream_t st);
+
 struct GemmArgs {
   const int8_t* Xq;
   const float* xs;

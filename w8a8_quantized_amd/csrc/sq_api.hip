@@ -100,6 +100,7 @@ const char* sq_status_string(sq_status status) {
     case SQ_ERR_DTYPE: return "SQ_ERR_DTYPE: dtype not accepted for this argument";
     case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
     case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime rejected a launch";
+    case SQ_ERR_ARG: return "SQ_ERR_ARG: an argument value is not accepted";
   }
   return "unknown sq_status";
 }
@@ -181,6 +182,26 @@ sq_status sq_quant_act_per_tensor(const void* X, sq_dtype x_t, int64_t T, int64_
   r = run_act_absmax(X, x_t, T, K, s, amax, 0, stream);
   if (r != SQ_OK) return r;
   return run_quant_static(X, x_t, T, K, s, amax, Xq, x_scale, stream);
+}
+
+sq_status sq_fold_norm_gain(const float* v, const float* s, int64_t K, float* out, hipStream_t stream) {
+  if (!v || !s || !out) return SQ_ERR_NULL;
+  if (K < 1) return SQ_ERR_SHAPE;
+  return hip_status(sq::launch_fold_gain(v, s, K, out, stream));
+}
+
+sq_status sq_norm_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, sq_norm kind,
+                            const float* gain, const float* bias, float eps, int8_t* Xq, float* x_scale,
+                            float* mean, float* rstd, hipStream_t stream) {
+  sq_status r = check_act_args(X, x_t, T, K);
+  if (r != SQ_OK) return r;
+  if (!gain || !Xq || !x_scale) return SQ_ERR_NULL;
+  if (kind != SQ_NORM_RMS && kind != SQ_NORM_LAYER) return SQ_ERR_ARG;
+  if (kind == SQ_NORM_RMS && bias) return SQ_ERR_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return SQ_ERR_ARG;
+  const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
+  return hip_status(sq::launch_norm_quant(X, x_t == SQ_BF16, kind == SQ_NORM_LAYER, T, K, gain, bias, eps,
+                                          Xq, x_scale, mean, rstd, vec, cu_count(), stream));
 }
 
 sq_status sq_w8a8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,

@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsq.so")
 
 SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
+SQ_NORM_RMS, SQ_NORM_LAYER = 0, 1
+_NORM = {"rms": SQ_NORM_RMS, "layer": SQ_NORM_LAYER}
 SQ_MAX_K = 133144
 _DT = {torch.float32: SQ_F32, torch.bfloat16: SQ_BF16, torch.int32: SQ_I32}
 
@@ -37,6 +39,8 @@ _SIGS = {
     "sq_act_absmax": ([_P, _I, _I64, _I64, _P, _P, _I, _P], _I),
     "sq_quant_act_static": ([_P, _I, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "sq_quant_act_per_tensor": ([_P, _I, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "sq_fold_norm_gain": ([_P, _P, _I64, _P, _P], _I),
+    "sq_norm_quant_act": ([_P, _I, _I64, _I64, _I, _P, _P, _F, _P, _P, _P, _P, _P], _I),
     "sq_w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_linear_workspace_size": ([_I64, _I64], _SZ),
     "sq_w8a8_linear": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
@@ -183,6 +187,34 @@ def sq_quant_act_per_tensor(X, s=None, amax=None, Xq=None, x_scale=None):
     _check(_lib.sq_quant_act_per_tensor(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(amax), _ptr(Xq),
                                         _ptr(x_scale), _stream(X.device)))
     return Xq, x_scale, amax
+
+
+def sq_fold_norm_gain(v, s, out=None):
+    """v / s per channel (a norm's gain or bias with the smoothing folded in)."""
+    if v.numel() != s.numel():
+        raise ValueError("v and s must have the same length")
+    out = _want(out, (v.numel(),), torch.float32, v.device)
+    _check(_lib.sq_fold_norm_gain(_ptr(v), _ptr(s), v.numel(), _ptr(out), _stream(v.device)))
+    return out
+
+
+def sq_norm_quant_act(X, kind, gain, bias=None, eps=1e-6, Xq=None, x_scale=None, mean=None,
+                      rstd=None):
+    """RMSNorm / LayerNorm (kind "rms" / "layer") with folded gain, then per-token
+    int8.  Returns (Xq, x_scale, mean, rstd)."""
+    T, K = X.shape
+    if kind not in _NORM:
+        raise ValueError(f"kind must be one of {tuple(_NORM)}")
+    if gain.numel() != K or (bias is not None and bias.numel() != K):
+        raise ValueError("gain and bias must have K entries")
+    Xq = _want(Xq, (T, K), torch.int8, X.device)
+    x_scale = _want(x_scale, (T,), torch.float32, X.device)
+    mean = _want(mean, (T,), torch.float32, X.device)
+    rstd = _want(rstd, (T,), torch.float32, X.device)
+    _check(_lib.sq_norm_quant_act(_ptr(X), _dt(X), T, K, _NORM[kind], _ptr(gain), _ptr(bias),
+                                  float(eps), _ptr(Xq), _ptr(x_scale), _ptr(mean), _ptr(rstd),
+                                  _stream(X.device)))
+    return Xq, x_scale, mean, rstd
 
 
 def sq_w8a8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
