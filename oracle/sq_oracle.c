@@ -239,6 +239,74 @@ void sqo_norm_apply(const float *X, int64_t T, int64_t K, int layer, const float
     }
 }
 
+/* Mixed-precision decomposition ([P4] "Decomposition: keep the outliers in
+ * high precision"; [P5] "Route it, or move it": the sum over K splits into the
+ * ordinary dimensions, run in int8, and the outlier dimensions, kept in full
+ * precision).  The outlier set is static, chosen once from calibration ([P4]:
+ * determined once and stored with the weights) as the n_o input channels with
+ * the largest absolute maximum ([P5]: dimensions ranked by max magnitude); ties
+ * go to the lower index.  Output: the chosen indices in ascending order. */
+static const float *g_sel_key;
+static int cmp_sel(const void *a, const void *b)
+{
+    int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+    if (g_sel_key[i] > g_sel_key[j]) return -1;
+    if (g_sel_key[i] < g_sel_key[j]) return 1;
+    return (i > j) - (i < j);
+}
+static int cmp_i32(const void *a, const void *b)
+{
+    int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+    return (i > j) - (i < j);
+}
+void sqo_decomp_select(const float *absmax, int64_t K, int64_t n_o, int32_t *idx)
+{
+    int32_t *ord = (int32_t *)malloc((size_t)K * sizeof(int32_t));
+    for (int64_t k = 0; k < K; ++k) ord[k] = (int32_t)k;
+    g_sel_key = absmax;
+    qsort(ord, (size_t)K, sizeof(int32_t), cmp_sel);
+    for (int64_t o = 0; o < n_o; ++o) idx[o] = ord[o];
+    qsort(idx, (size_t)n_o, sizeof(int32_t), cmp_i32);
+    free(ord);
+}
+
+/* The ordinary ("bulk") columns of A [rows x K], in order, and the outlier
+ * columns listed in idx, as two compact matrices ([P4]: x[keep], x[outlier_idx]). */
+void sqo_decomp_split(const float *A, int64_t rows, int64_t K, const int32_t *idx, int64_t n_o,
+                      float *bulk, float *outl)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t o = 0, b = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            if (o < n_o && idx[o] == k) outl[r * n_o + o++] = A[r * K + k];
+            else bulk[r * (K - n_o) + b++] = A[r * K + k];
+        }
+    }
+}
+
+/* The full-precision part: y_out[t][n] = sum over o (ascending) of
+ * Xo[t][o] * Wo[n][o], binary32, one rounding per multiply and per add, from 0. */
+void sqo_decomp_outlier_product(const float *Xo, const float *Wo, int64_t T, int64_t N, int64_t n_o,
+                                float *Yo)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t o = 0; o < n_o; ++o) {
+                float p = Xo[t * n_o + o] * Wo[n * n_o + o];
+                acc = acc + p;
+            }
+            Yo[t * N + n] = acc;
+        }
+}
+
+/* y = y_bulk + y_out, one binary32 addition. */
+void sqo_add(const float *a, const float *b, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = a[i] + b[i];
+}
+
 /* Integer matmul.  [P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk.
  * Accumulated in int64; returns 1 if any sum does not fit int32, else 0. */
 int sqo_int_gemm(const int8_t *Xq, const int8_t *Wq, int64_t T, int64_t N, int64_t K,

@@ -34,7 +34,9 @@ __all__ = ["build", "col_absmax", "smooth_scales", "quantize_weights", "quant_ac
            "int_gemm", "int_gemm_at", "dequant", "dequant_at", "to_bf16", "w8a8_linear",
            "prepare", "w8a8_relative_error", "channel_max_over_median", "exact_product",
            "widen_bf16", "set_threads", "act_tensor_absmax", "quant_act_static",
-           "quant_act_per_tensor", "fold_gain", "norm_stats", "norm_apply", "norm_quant_act"]
+           "quant_act_per_tensor", "fold_gain", "norm_stats", "norm_apply", "norm_quant_act",
+           "decomp_select", "decomp_split", "decomp_outlier_product", "decomp_prepare",
+           "decomp_linear", "decomp_relative_error"]
 
 GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
              "-std=c11", "-Wall"]
@@ -78,6 +80,12 @@ def _load():
             lib.sqo_norm_stats.argtypes = [P, I64, I64, ctypes.c_int, F, P, P]
             lib.sqo_norm_apply.argtypes = [P, I64, I64, ctypes.c_int, P, P, P, P, P]
             for f in ("sqo_fold_gain", "sqo_norm_stats", "sqo_norm_apply"):
+                getattr(lib, f).restype = None
+            lib.sqo_decomp_select.argtypes = [P, I64, I64, P]
+            lib.sqo_decomp_split.argtypes = [P, I64, I64, P, I64, P, P]
+            lib.sqo_decomp_outlier_product.argtypes = [P, P, I64, I64, I64, P]
+            lib.sqo_add.argtypes = [P, P, I64, P]
+            for f in ("sqo_decomp_select", "sqo_decomp_split", "sqo_decomp_outlier_product", "sqo_add"):
                 getattr(lib, f).restype = None
             for f in ("sqo_col_absmax", "sqo_smooth_scales", "sqo_quantize_weights",
                       "sqo_quant_act", "sqo_dequant", "sqo_dequant_at", "sqo_to_bf16"):
@@ -234,6 +242,72 @@ def norm_quant_act(X, kind, gain, bias=None, eps=1e-6, stats=None):
     H = norm_apply(X, kind, mean, rstd, gain, bias)
     Xq, xs = quant_act(H, None)
     return Xq, xs, mean, rstd
+
+
+def decomp_select(absmax, n_o):
+    """[P4] "Decomposition" (a static outlier set chosen from calibration); [P5]
+    (dimensions ranked by max magnitude): the n_o input channels with the largest
+    absolute maximum, ties to the lower index, returned in ascending order."""
+    a = _f32(absmax)
+    assert 0 <= n_o <= a.size
+    idx = np.empty(n_o, np.int32)
+    _load().sqo_decomp_select(_ptr(a), a.size, int(n_o), _ptr(idx))
+    return idx
+
+
+def decomp_split(A, idx):
+    """(A[:, keep], A[:, idx]) with keep the complement of idx, both in order."""
+    A = _f32(A)
+    rows, K = A.shape
+    idx = np.ascontiguousarray(idx, np.int32)
+    assert np.all(np.diff(idx) > 0) and (idx.size == 0 or (idx[0] >= 0 and idx[-1] < K))
+    bulk = np.empty((rows, K - idx.size), np.float32)
+    outl = np.empty((rows, idx.size), np.float32)
+    _load().sqo_decomp_split(_ptr(A), rows, K, _ptr(idx), idx.size, _ptr(bulk), _ptr(outl))
+    return bulk, outl
+
+
+def decomp_outlier_product(Xo, Wo):
+    """[P4] y_out = x_out @ W_out.T in binary32 (sum over the outlier channels in
+    ascending order, one rounding per operation)."""
+    Xo, Wo = _f32(Xo), _f32(Wo)
+    T, n_o = Xo.shape
+    N, n_o2 = Wo.shape
+    assert n_o == n_o2
+    Yo = np.empty((T, N), np.float32)
+    _load().sqo_decomp_outlier_product(_ptr(Xo), _ptr(Wo), T, N, n_o, _ptr(Yo))
+    return Yo
+
+
+def decomp_prepare(W, idx):
+    """Offline half: bulk weight columns quantised per output channel; outlier
+    columns kept in binary32.  Returns (Wq_bulk, w_scale, W_out)."""
+    Wb, Wo = decomp_split(W, idx)
+    Wq, ws = quantize_weights(Wb, None)
+    return Wq, ws, Wo
+
+
+def decomp_linear(X, idx, Wq_bulk, w_scale, W_out):
+    """Runtime half ([P4] split_outlier_matmul; [P5] split reduction): bulk
+    activation columns quantised per token, integer matmul with the float
+    epilogue, plus the binary32 product of the outlier columns, added once.
+    Returns (y float32 [T,N], Xq_bulk, x_scale, X_out, acc)."""
+    Xb, Xo = decomp_split(X, idx)
+    Xq, xs = quant_act(Xb, None)
+    acc = int_gemm(Xq, Wq_bulk)
+    yb = dequant(acc, xs, w_scale)
+    yo = decomp_outlier_product(Xo, W_out)
+    y = np.empty_like(yb)
+    _load().sqo_add(_ptr(yb), _ptr(yo), yb.size, _ptr(y))
+    return y, Xq, xs, Xo, acc
+
+
+def decomp_relative_error(X, W, idx):
+    """||Y_decomp - Y|| / ||Y|| against the exact float64 product."""
+    Wq, ws, Wo = decomp_prepare(W, idx)
+    y, *_ = decomp_linear(X, idx, Wq, ws, Wo)
+    Y = exact_product(X, W)
+    return float(np.linalg.norm(y.astype(np.float64) - Y) / np.linalg.norm(Y))
 
 
 def int_gemm(Xq, Wq):

@@ -558,3 +558,84 @@ def test_fold_gain_is_division():
     g = rng.uniform(-2, 2, 1000).astype(np.float32)
     s = rng.uniform(0.01, 50, 1000).astype(np.float32)
     assert np.array_equal(O.fold_gain(g, s), (g / s).astype(np.float32))
+
+
+# ------------------------------------------- mixed-precision decomposition (P4, P5)
+def _planted(seed, T=512, K=256, N=128, dims=(7, 23, 88, 154, 201), mult=14.0):
+    """The structure of the maitreyasuin page's synthetic tensor (section "Route
+    it, or move it"): standard-normal activations with a few input dimensions
+    multiplied in every token, weights N(0, 0.1^2); drawn from our own stream."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    X[:, list(dims)] *= np.float32(mult)
+    W = (rng.standard_normal((N, K)) * 0.1).astype(np.float32)
+    return X, W, np.array(sorted(dims), np.int32)
+
+
+def test_decomp_select_ranks_by_max_magnitude():
+    """maitreyasuin page: ranking dimensions by max magnitude recovers the planted
+    ones; ties go to the lower index; the result is in ascending order."""
+    X, _, dims = _planted(41)
+    idx = O.decomp_select(O.col_absmax(X), 5)
+    assert idx.tolist() == dims.tolist()
+    a = np.array([1, 5, 3, 5, 5, 0.5], np.float32)
+    assert O.decomp_select(a, 2).tolist() == [1, 3]
+    assert O.decomp_select(a, 4).tolist() == [1, 2, 3, 4]
+    assert O.decomp_select(a, 0).size == 0
+
+
+def test_decomp_split_is_exact():
+    """mercemay.com page, "Decomposition": the two products add up to the product
+    of the concatenated operands (float64)."""
+    X, W, dims = _planted(42, T=64)
+    Xb, Xo = O.decomp_split(X, dims)
+    Wb, Wo = O.decomp_split(W, dims)
+    keep = np.setdiff1d(np.arange(X.shape[1]), dims)
+    assert np.array_equal(Xb, X[:, keep]) and np.array_equal(Xo, X[:, dims])
+    y = Xb.astype(np.float64) @ Wb.astype(np.float64).T + Xo.astype(np.float64) @ Wo.astype(np.float64).T
+    Y = O.exact_product(X, W)
+    assert np.linalg.norm(y - Y) <= 1e-12 * np.linalg.norm(Y)
+
+
+def test_decomp_without_outliers_is_plain_w8a8():
+    X, W, _ = _planted(43, T=40)
+    none = np.zeros(0, np.int32)
+    Wq, ws, Wo = O.decomp_prepare(W, none)
+    y, Xq, xs, Xo, acc = O.decomp_linear(X, none, Wq, ws, Wo)
+    y2, Xq2, xs2, acc2 = O.w8a8_linear(X, None, *O.quantize_weights(W, None))
+    assert np.array_equal(y, y2) and np.array_equal(Xq, Xq2) and np.array_equal(acc, acc2)
+
+
+def test_decomp_all_outliers_is_float_product():
+    """Every channel kept in full precision: the layer is the binary32 product,
+    within the recursive-summation bound K * 2^-24 * sum |x w| of the exact one."""
+    X, W, _ = _planted(44, T=30, K=64, N=20, dims=(1, 2))
+    idx = np.arange(64, dtype=np.int32)
+    Wq, ws, Wo = O.decomp_prepare(W, idx)
+    assert Wq.shape == (20, 0)
+    y, *_ = O.decomp_linear(X, idx, Wq, ws, Wo)
+    Y = O.exact_product(X, W)
+    bound = 64 * 2.0 ** -24 * (np.abs(X).astype(np.float64) @ np.abs(W).astype(np.float64).T)
+    assert np.all(np.abs(y - Y) <= bound)
+    assert np.abs(y - Y).max() > 0     # it is a binary32 sum, not the exact one
+
+
+def test_decomp_bulk_scale_ignores_outliers():
+    X = np.zeros((2, 16), np.float32)
+    X[0, 3] = 1000.0      # outlier channel
+    X[0, 5] = 1.27
+    X[1, 3] = -2.0
+    idx = np.array([3], np.int32)
+    Xb, Xo = O.decomp_split(X, idx)
+    Xq, xs = O.quant_act(Xb, None)
+    assert xs[0] == np.float32(np.float32(1.27) / np.float32(127)) and xs[1] == 1.0
+    assert Xo[:, 0].tolist() == [1000.0, -2.0]
+
+
+def test_decomp_beats_one_grid():
+    """[P5] "Route it, or move it" (105.4x on its own draw) and [P4]: keeping the
+    planted dimensions in full precision cuts the W8A8 error by a large factor."""
+    X, W, dims = _planted(45)
+    plain = O.w8a8_relative_error(X, W, None)
+    split = O.decomp_relative_error(X, W, O.decomp_select(O.col_absmax(X), 5))
+    assert split * 4 < plain
