@@ -152,6 +152,63 @@ def decode_measure(sq, torch, reps=30):
             "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": byts, "weight_copies_rotated": 3}
 
 
+def _time_calls(torch, fn, copies, reps=20):
+    """Per-call time (ms) of `reps` back-to-back calls cycling through `copies`,
+    queued behind a GPU-side wait so that host launch time is not measured."""
+    for i in range(3):
+        fn(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    a.record()
+    for i in range(reps):
+        fn(copies[i % len(copies)])
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def decomp_measure(sq, torch):
+    """Mixed-precision decomposition on the two workloads with planted outlier
+    channels (their count taken as the static set, chosen from the calibration
+    draw), next to the smoothed per-token path on the same shapes."""
+    import workloads as WL
+    dev = torch.device("cuda")
+    out = {}
+    for name, n_o in (("prefill_t2048_k4096_n16384", 8), ("decode_t16_k8192_n28672", 41)):
+        w = WL.make(name)
+        T, N, K = w.T, w.N, w.K
+        X = torch.from_numpy(w.X).to(torch.bfloat16).to(dev)
+        Xc = torch.from_numpy(w.X_calib).to(torch.bfloat16).to(dev)
+        W = torch.from_numpy(w.W).to(dev)
+        idx, mask = sq.sq_decomp_select(sq.sq_col_absmax(Xc), n_o)
+        Wq_d, ws_d, Wo = sq.sq_decomp_prepare_weights(W, mask, idx)
+        s, _, _ = sq.sq_smooth_scales(Xc, W, w.alpha)
+        Wq_s, ws_s = sq.sq_quantize_weights(W, s)
+        del W
+        torch.cuda.empty_cache()
+        # decode: rotate three copies of the weights (more than the Infinity Cache)
+        nc = 3 if T <= 64 else 1
+        Wd = [Wq_d] + [Wq_d.clone() for _ in range(nc - 1)]
+        Ws = [Wq_s] + [Wq_s.clone() for _ in range(nc - 1)]
+        Xq_d, xs_d, Xo = sq.sq_decomp_quant_act(X, mask, idx)
+        Xq_s, xs_s = sq.sq_quant_act(X, s)
+        Y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        t_qd = _time_calls(torch, lambda _: sq.sq_decomp_quant_act(X, mask, idx, Xq=Xq_d, x_scale=xs_d, X_out=Xo), [None])
+        t_qs = _time_calls(torch, lambda _: sq.sq_quant_act(X, s, Xq=Xq_s, x_scale=xs_s), [None])
+        t_gd = _time_calls(torch, lambda wq: sq.sq_decomp_gemm(Xq_d, xs_d, wq, ws_d, Xo, Wo, Y=Y), Wd)
+        t_gs = _time_calls(torch, lambda wq: sq.sq_w8a8_gemm(Xq_s, xs_s, wq, ws_s, Y=Y), Ws)
+        ops = 2.0 * T * N * K
+        out[name] = {"n_outliers": n_o,
+                     "decomp_quant_act_us": t_qd * 1e3, "smooth_quant_act_us": t_qs * 1e3,
+                     "decomp_gemm_us": t_gd * 1e3, "smooth_gemm_us": t_gs * 1e3,
+                     "decomp_linear_TOPS": ops / ((t_qd + t_gd) * 1e-3) / 1e12,
+                     "smooth_linear_TOPS": ops / ((t_qs + t_gs) * 1e-3) / 1e12}
+        del Wd, Ws, Wq_d, Wq_s, X, Xc, Y
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +352,7 @@ def main():
         del X, Xs, W, Wq, Xq, Y
         torch.cuda.empty_cache()
         out["decode_gemm"] = decode_measure(sq, torch)
+        out["decomposition"] = decomp_measure(sq, torch)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -241,6 +241,68 @@ sq_status sq_norm_quant_act(const void *X, sq_dtype x_t, int64_t T, int64_t K, s
                             float *x_scale, float *mean, float *rstd, hipStream_t stream);
 
 /*
+ * Mixed-precision decomposition, the alternative to smoothing (mercemay.com
+ * "Activation Outlier Channels and Mixed-Precision Decomposition", section
+ * "Decomposition: keep the outliers in high precision"; maitreyasuin page,
+ * "Route it, or move it"): the sum over K splits into the bulk channels, run in
+ * int8 with per-token / per-output-channel scales, and a few outlier channels
+ * kept in binary32:
+ *     Y[t][n] = fl32(acc_bulk[t][n] * fl32(x_scale[t] * w_scale[n]))
+ *               + (sum over o ascending of X[t][idx[o]] * W[n][idx[o]], binary32)
+ * The outlier set is static (chosen once from calibration).  The int8 operands
+ * keep their full width with the outlier columns zeroed, so the bulk scales
+ * ignore the outliers and the GEMM main loop is the ordinary one.  No smoothing
+ * is applied on this path.
+ *
+ * sq_decomp_select: the n_o input channels with the largest absmax (for example
+ * calibration column maxima from sq_col_absmax), ties to the lower index
+ * (maitreyasuin page: dimensions ranked by max magnitude).
+ *   absmax  device float [K];  0 <= n_o <= K
+ *   idx     device int32 [n_o], written: the chosen channels, ascending
+ *   mask    device float [K], written: 0 at the chosen channels, 1 elsewhere
+ */
+sq_status sq_decomp_select(const float *absmax, int64_t K, int64_t n_o, int32_t *idx, float *mask,
+                           hipStream_t stream);
+
+/*
+ * Offline weight side: Wq = per-output-channel int8 of W with the outlier columns
+ * zeroed (w_scale from the bulk columns only), W_out[o][n] = W[n][idx[o]] in
+ * binary32 (bf16 widened exactly).
+ *   W        device, w_t = SQ_F32 or SQ_BF16, [N][K]
+ *   mask, idx, n_o   from sq_decomp_select (idx ascending, entries in [0, K);
+ *            an entry outside that range reads as a zero column)
+ *   Wq       device int8 [N][K], written;  w_scale  device float [N], written
+ *   W_out    device float [n_o][N], written (may be NULL when n_o = 0)
+ */
+sq_status sq_decomp_prepare_weights(const void *W, sq_dtype w_t, int64_t N, int64_t K,
+                                    const float *mask, const int32_t *idx, int64_t n_o,
+                                    int8_t *Wq, float *w_scale, float *W_out, hipStream_t stream);
+
+/*
+ * Run-time activation side: Xq = per-token int8 of X with the outlier columns
+ * zeroed (x_scale from the bulk columns only), X_out[o][t] = X[t][idx[o]] in
+ * binary32.  X is read once by the quantiser; the outlier columns are gathered
+ * by a second, small launch.
+ *   X        device, x_t = SQ_F32 or SQ_BF16, [T][K]
+ *   Xq       device int8 [T][K], written;  x_scale  device float [T], written
+ *   X_out    device float [n_o][T], written (may be NULL when n_o = 0)
+ */
+sq_status sq_decomp_quant_act(const void *X, sq_dtype x_t, int64_t T, int64_t K,
+                              const float *mask, const int32_t *idx, int64_t n_o,
+                              int8_t *Xq, float *x_scale, float *X_out, hipStream_t stream);
+
+/*
+ * The decomposed layer's GEMM: sq_w8a8_gemm on the bulk operands with the
+ * binary32 outlier product added in the epilogue (no second launch, no second
+ * output pass).  y_t = SQ_F32 or SQ_BF16 (bf16 is the RNE rounding of the
+ * binary32 sum).  X_out and W_out must be 16-byte aligned (SQ_ERR_ARG).
+ */
+sq_status sq_decomp_gemm(const int8_t *Xq, const float *x_scale, const int8_t *Wq,
+                         const float *w_scale, const float *X_out, const float *W_out,
+                         int64_t T, int64_t N, int64_t K, int64_t n_o, void *Y, sq_dtype y_t,
+                         hipStream_t stream);
+
+/*
  * W8A8 GEMM with int32 accumulation and the dequantising epilogue
  * (mercemay.com "Activation Outlier Channels and Mixed-Precision Decomposition",
  * section "Decomposition": integer matmul, float epilogue multiplying by the

@@ -160,3 +160,23 @@ def test_norm_arguments(lib):
     assert call(kind=0, b=FAKE) == SQ_ERR_ARG          # RMSNorm has no bias
     for eps in (-1e-6, float("nan"), float("inf")):
         assert call(eps=eps) == SQ_ERR_ARG
+
+
+def test_decomp_arguments(lib):
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.sq_decomp_select.argtypes = [P, I64, I64, P, P, P]
+    lib.sq_decomp_prepare_weights.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, P]
+    lib.sq_decomp_quant_act.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, P]
+    lib.sq_decomp_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, I, P]
+    assert lib.sq_decomp_select(FAKE, 16, 2, None, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_decomp_select(FAKE, 16, 17, FAKE, FAKE, None) == SQ_ERR_SHAPE
+    assert lib.sq_decomp_select(FAKE, 16, -1, FAKE, FAKE, None) == SQ_ERR_SHAPE
+    assert lib.sq_decomp_prepare_weights(FAKE, F32, 4, 16, FAKE, FAKE, 2, FAKE, FAKE, None, None) == SQ_ERR_NULL
+    assert lib.sq_decomp_prepare_weights(FAKE, I32, 4, 16, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None) == SQ_ERR_DTYPE
+    assert lib.sq_decomp_quant_act(FAKE, BF16, 4, 16, None, FAKE, 2, FAKE, FAKE, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_decomp_quant_act(FAKE, BF16, 4, 16, FAKE, FAKE, 20, FAKE, FAKE, FAKE, None) == SQ_ERR_SHAPE
+    # raw accumulators have no outlier term; outlier columns must be 16-byte aligned
+    assert lib.sq_decomp_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 16, 2, FAKE, I32, None) == SQ_ERR_DTYPE
+    assert lib.sq_decomp_gemm(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 4, 16, 2, FAKE, F32, None) == SQ_ERR_NULL
+    assert lib.sq_decomp_gemm(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004), FAKE, 4, 4, 16, 2, FAKE, F32,
+                              None) == SQ_ERR_ARG

@@ -26,7 +26,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["sq_api.hip", "k_reduce.hip", "k_quant.hip", "k_norm.hip", "k_gemm.hip", "k_gemv.hip"]
+SOURCES = ["sq_api.hip", "k_reduce.hip", "k_quant.hip", "k_norm.hip", "k_decomp.hip", "k_gemm.hip",
+           "k_gemv.hip"]
 
 
 def _compile(src: str) -> str:

@@ -62,6 +62,47 @@ __device__ __forceinline__ void store4(void* Y, int64_t off, int nrem, const int
   }
 }
 
+// so[e] += sum over o ascending of x[o * ldx] * w[o * ldw + e], e = 0..3, one
+// binary32 rounding per multiply and per add (the outlier-channel product of the
+// mixed-precision decomposition).  Loads are issued OC outliers at a time, ahead
+// of the dependent additions; w + o * ldw must be 16-byte aligned.
+template <int OC>
+__device__ __forceinline__ void outlier_sum4(const float* __restrict__ x, int64_t ldx,
+                                             const float* __restrict__ w, int64_t ldw, int n_o,
+                                             float* so) {
+  for (int o0 = 0; o0 < n_o; o0 += OC) {
+    float xv[OC];
+    float4 w4[OC];
+#pragma unroll
+    for (int u = 0; u < OC; ++u) {
+      const bool in = o0 + u < n_o;
+      xv[u] = in ? x[(int64_t)(o0 + u) * ldx] : 0.0f;
+      w4[u] = in ? *reinterpret_cast<const float4*>(w + (int64_t)(o0 + u) * ldw) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < OC; ++u) {
+      if (o0 + u < n_o) {
+        so[0] = so[0] + xv[u] * w4[u].x;
+        so[1] = so[1] + xv[u] * w4[u].y;
+        so[2] = so[2] + xv[u] * w4[u].z;
+        so[3] = so[3] + xv[u] * w4[u].w;
+      }
+    }
+  }
+}
+
+// Element stores of the nrem (>= 1) outputs that exist, each the dequantised
+// value plus its outlier-channel product (float outputs only).
+template <int OUT>
+__device__ __forceinline__ void store4o(void* Y, int64_t off, int nrem, const int* a, float sc_t,
+                                        const float* wsv, const float* so) {
+  for (int e = 0; e < 4 && e < nrem; ++e) {
+    const float v = (float)a[e] * (sc_t * wsv[e]) + so[e];
+    if (OUT == kOutF32) static_cast<float*>(Y)[off + e] = v;
+    else static_cast<uint16_t*>(Y)[off + e] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
 // Tile order: XCD-contiguous runs, then groups of 8 output-channel tiles.
 __device__ __forceinline__ void tile_coords(int bid, int G, int tiles_n, int tiles_t, int& tn, int& tt) {
   const int xcd = bid & 7, idx = bid >> 3;
@@ -96,11 +137,17 @@ constexpr int kLgkm0 = ~0x0F00;
 // Epilogue (VEC).  Each wave stages 32 token rows x WTN outputs at a time in
 // LDS (rows padded by 16 bytes) and writes them back as row-contiguous 16-byte
 // stores, so every store instruction covers whole 256/512-byte row segments.
-template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC>
+//
+// OUTL (mixed-precision decomposition, mercemay.com "Activation Outlier Channels
+// and Mixed-Precision Decomposition", section "Decomposition"): the float
+// epilogue value gets the binary32 product of the outlier channels added,
+//   y = fl32(fl32(acc) * fl32(xs * ws)) + (sum over o ascending of xo[o][t] * wo[o][n]).
+template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC, bool OUTL>
 __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy,
-    int tiles_n, int tiles_t) {
+    int tiles_n, int tiles_t, const float* __restrict__ xo, int64_t ldxo,
+    const float* __restrict__ wo, int64_t ldwo, int n_o) {
   // The body exists only in the device pass (the host pass needs just the
   // launch stub, and its front end cannot take the device scheduling builtins).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -267,8 +314,10 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     constexpr int RPI = 64 / CPRO;             // output rows per wave instruction
     static_assert(NW * 32 * ROWB <= STAGES * STAGE_BYTES, "epilogue staging does not fit");
     int8_t* E = lds + wave * (32 * ROWB);
+    // channel scales held across the token blocks (re-read per block instead
+    // when the outlier term needs the registers)
     float wsq[RN][4][4];
-    if (OUT != kOutI32) {
+    if (OUT != kOutI32 && !OUTL) {
 #pragma unroll
       for (int i = 0; i < RN; ++i)
 #pragma unroll
@@ -297,7 +346,21 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
             } else {
               float v[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = (float)acc[i][j][4 * g + e] * (sc * wsq[i][g][e]);
+              for (int e = 0; e < 4; ++e) {
+                if (OUTL) {
+                  const int nw = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
+                  wsq[i][g][e] = nw < N ? ws[nw + e] : 0.0f;
+                }
+                v[e] = (float)acc[i][j][4 * g + e] * (sc * wsq[i][g][e]);
+              }
+              if (OUTL) {
+                const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
+                float so[4] = {0.f, 0.f, 0.f, 0.f};
+                // chunks of 4 keep the 16-wave tile within its 128 registers
+                if (t_l < T && n < N) outlier_sum4<(NW > 8 ? 4 : 8)>(xo + t_l, ldxo, wo + n, ldwo, n_o, so);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = v[e] + so[e];
+              }
               if (OUT == kOutF32) {
                 *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
               } else {
@@ -335,7 +398,17 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
           float wsv[4] = {0.f, 0.f, 0.f, 0.f};
           if (OUT != kOutI32)
             for (int e = 0; e < 4; ++e) wsv[e] = (n + e < N) ? ws[n + e] : 0.0f;
-          store4<OUT, false>(Y, (int64_t)t * ldy + n, N - n, a4, sc, wsv);
+          if (OUTL) {
+            float so[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int o = 0; o < n_o; ++o) {
+              const float xv = xo[(int64_t)o * ldxo + t];
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) so[e] = so[e] + xv * wo[(int64_t)o * ldwo + n + e];
+            }
+            store4o<OUT>(Y, (int64_t)t * ldy + n, N - n, a4, sc, wsv, so);
+          } else {
+            store4<OUT, false>(Y, (int64_t)t * ldy + n, N - n, a4, sc, wsv);
+          }
         }
       }
     }
@@ -344,23 +417,25 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
 }
 
 template <int BN, int BT, int BK, int WN, int WT, int ST, bool VEC>
-static void launch_out(int out, dim3 grid, dim3 block, hipStream_t st, const int8_t* Xq, const float* xs,
-                       const int8_t* Wq, const float* ws, int T, int N, int K, void* Y, int64_t ldy,
-                       int tiles_n, int tiles_t) {
+static void launch_out(int out, bool outl, dim3 grid, dim3 block, hipStream_t st, const int8_t* Xq,
+                       const float* xs, const int8_t* Wq, const float* ws, int T, int N, int K, void* Y,
+                       int64_t ldy, int tiles_n, int tiles_t, const float* xo, int64_t ldxo, const float* wo,
+                       int64_t ldwo, int n_o) {
+#define SQ_GEMM_LAUNCH(O, L)                                                                                  \
+  hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, O, VEC, L>), grid, block, 0, st, Xq, xs, Wq, \
+                     ws, T, N, K, Y, ldy, tiles_n, tiles_t, xo, ldxo, wo, ldwo, n_o)
   switch (out) {
     case kOutF32:
-      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, kOutF32, VEC>), grid, block, 0, st, Xq, xs, Wq,
-                         ws, T, N, K, Y, ldy, tiles_n, tiles_t);
+      if (outl) SQ_GEMM_LAUNCH(kOutF32, true); else SQ_GEMM_LAUNCH(kOutF32, false);
       break;
     case kOutBF16:
-      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, kOutBF16, VEC>), grid, block, 0, st, Xq, xs, Wq,
-                         ws, T, N, K, Y, ldy, tiles_n, tiles_t);
+      if (outl) SQ_GEMM_LAUNCH(kOutBF16, true); else SQ_GEMM_LAUNCH(kOutBF16, false);
       break;
     default:
-      hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, kOutI32, VEC>), grid, block, 0, st, Xq, xs, Wq,
-                         ws, T, N, K, Y, ldy, tiles_n, tiles_t);
+      SQ_GEMM_LAUNCH(kOutI32, false);
       break;
   }
+#undef SQ_GEMM_LAUNCH
 }
 
 template <int BN, int BT, int BK, int WN, int WT, int ST>
@@ -381,6 +456,9 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
       const int8_t* Wq = a.Wq + nb * a.K;
       const float* xs = a.xs ? a.xs + tb : nullptr;
       const float* ws = a.ws ? a.ws + nb : nullptr;
+      const bool outl = a.n_o > 0 && a.out != kOutI32;
+      const float* xo = outl ? a.xo + tb : nullptr;
+      const float* wo = outl ? a.wo + nb : nullptr;
       void* Y = static_cast<char*>(a.Y) + (tb * a.N + nb) * osz;
       // a column slice of Y keeps 16-byte alignment only if nb is a multiple of 4
       // the LDS-staged epilogue writes 16-byte row chunks: N must be a multiple of
@@ -388,8 +466,10 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
       const int per16 = a.out == kOutBF16 ? 8 : 4;
       const bool vs = a.vec_store && a.N % per16 == 0 && nb % per16 == 0;
       const int K = (int)a.K;
-      if (vs) launch_out<BN, BT, BK, WN, WT, ST, true>(a.out, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N, tiles_n, tiles_t);
-      else launch_out<BN, BT, BK, WN, WT, ST, false>(a.out, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N, tiles_n, tiles_t);
+      if (vs) launch_out<BN, BT, BK, WN, WT, ST, true>(a.out, outl, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N,
+                                                        tiles_n, tiles_t, xo, a.T, wo, a.N, (int)a.n_o);
+      else launch_out<BN, BT, BK, WN, WT, ST, false>(a.out, outl, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N,
+                                                     tiles_n, tiles_t, xo, a.T, wo, a.N, (int)a.n_o);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -412,7 +492,9 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const int8_t* __restr
                                                            const float* __restrict__ xs,
                                                            const int8_t* __restrict__ Wq,
                                                            const float* __restrict__ ws, int64_t T,
-                                                           int64_t N, int64_t K, void* __restrict__ Y) {
+                                                           int64_t N, int64_t K, void* __restrict__ Y,
+                                                           const float* __restrict__ xo,
+                                                           const float* __restrict__ wo, int64_t n_o) {
   const int64_t total = T * N;
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (int64_t)gridDim.x * blockDim.x) {
@@ -424,7 +506,12 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const int8_t* __restr
     if (OUT == kOutI32) {
       static_cast<int*>(Y)[o] = acc;
     } else {
-      const float v = (float)acc * (xs[t] * ws[n]);
+      float v = (float)acc * (xs[t] * ws[n]);
+      if (n_o > 0) {
+        float so = 0.0f;
+        for (int64_t q = 0; q < n_o; ++q) so = so + xo[q * T + t] * wo[q * N + n];
+        v = v + so;
+      }
       if (OUT == kOutF32) static_cast<float*>(Y)[o] = v;
       else static_cast<uint16_t*>(Y)[o] = (uint16_t)f32_to_bf16(v);
     }
@@ -438,13 +525,16 @@ hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st) {
   dim3 grid((unsigned)g), block(256);
   switch (a.out) {
     case kOutF32:
-      hipLaunchKernelGGL(gemm_generic_kernel<kOutF32>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y);
+      hipLaunchKernelGGL(gemm_generic_kernel<kOutF32>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y,
+                         a.xo, a.wo, a.out == kOutI32 ? 0 : a.n_o);
       break;
     case kOutBF16:
-      hipLaunchKernelGGL(gemm_generic_kernel<kOutBF16>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y);
+      hipLaunchKernelGGL(gemm_generic_kernel<kOutBF16>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y,
+                         a.xo, a.wo, a.out == kOutI32 ? 0 : a.n_o);
       break;
     default:
-      hipLaunchKernelGGL(gemm_generic_kernel<kOutI32>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y);
+      hipLaunchKernelGGL(gemm_generic_kernel<kOutI32>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y,
+                         a.xo, a.wo, a.out == kOutI32 ? 0 : a.n_o);
       break;
   }
   return hipGetLastError();

@@ -42,10 +42,13 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 
 // Requires K % 16 == 0, N * K < 2^31 and T * K < 2^31 (the host splits larger N),
 // 16-byte aligned Xq and Wq.  KW waves per workgroup, which owns NB*16 channels.
-template <int NB, int TB, int OUT, int KW>
+// OUTL: the epilogue adds the binary32 outlier-channel product of the
+// mixed-precision decomposition, sum over o ascending of xo[o][t] * wo[o][n].
+template <int NB, int TB, int OUT, int KW, bool OUTL>
 __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
-    const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy, int vec_store) {
+    const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy, int vec_store,
+    const float* __restrict__ xo, int64_t ldxo, const float* __restrict__ wo, int64_t ldwo, int n_o) {
   // The body exists only in the device pass (the host pass needs just the stub).
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = 256;                 // K bytes per chunk
@@ -170,6 +173,35 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (sc * ws[n + e]) : 0.0f;
+      if (OUTL) {
+        // binary32 outlier-channel product, o ascending; loads 8 outliers ahead
+        float so[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int o0 = 0; o0 < n_o; o0 += 8) {
+          float xv[8], wv[8][4];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const bool in = o0 + u < n_o;
+            const int64_t ro = (int64_t)(o0 + u);
+            xv[u] = in ? xo[ro * ldxo + t] : 0.0f;
+            if (in && vec) {
+              const float4 w4 = *reinterpret_cast<const float4*>(wo + ro * ldwo + n);
+              wv[u][0] = w4.x; wv[u][1] = w4.y; wv[u][2] = w4.z; wv[u][3] = w4.w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) wv[u][e] = (in && e < nrem) ? wo[ro * ldwo + n + e] : 0.0f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (o0 + u < n_o) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (e < nrem) so[e] = so[e] + xv[u] * wv[u][e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = v[e] + so[e];
+      }
       if (OUT == kOutF32) {
         float* y = static_cast<float*>(Y) + (int64_t)t * ldy + n;
         if (vec) *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
@@ -204,17 +236,24 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
     void* Y = static_cast<char*>(a.Y) + nb * osz;
     const int vs = (a.vec_store && nb % 4 == 0) ? 1 : 0;
     const int T = (int)a.T, K = (int)a.K;
+    const bool outl = a.n_o > 0 && a.out != kOutI32;
+    const float* wo = outl ? a.wo + nb : nullptr;
+    const int n_o = outl ? (int)a.n_o : 0;
+#define SQ_GEMV_LAUNCH(O, L)                                                                           \
+  hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, O, KW, L>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, \
+                     a.N, vs, a.xo, a.T, wo, a.N, n_o)
     switch (a.out) {
       case kOutF32:
-        hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutF32, KW>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs);
+        if (outl) SQ_GEMV_LAUNCH(kOutF32, true); else SQ_GEMV_LAUNCH(kOutF32, false);
         break;
       case kOutBF16:
-        hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutBF16, KW>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs);
+        if (outl) SQ_GEMV_LAUNCH(kOutBF16, true); else SQ_GEMV_LAUNCH(kOutBF16, false);
         break;
       default:
-        hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, kOutI32, KW>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs);
+        SQ_GEMV_LAUNCH(kOutI32, false);
         break;
     }
+#undef SQ_GEMV_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

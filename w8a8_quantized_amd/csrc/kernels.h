@@ -19,8 +19,9 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
                                 hipStream_t st);
 // Row quantiser modes: per-token activations (divide by s, per-row range),
-// per-output-channel weights (multiply by s, per-row range), activations against
-// the range *clip (divide by s, one scale for every row).
+// per-output-channel weights (multiply by s, per-row range; also the
+// decomposition's bulk rows, with s a 0/1 column mask), activations against the
+// range *clip (divide by s, one scale for every row).
 enum QuantMode { kQuantAct = 0, kQuantWeights = 1, kQuantActStatic = 2 };
 hipError_t launch_quant_rows(const void* A, bool bf16, int mode, int64_t R, int64_t K,
                              const float* s, const float* clip, int8_t* Q, float* scale,
@@ -34,6 +35,13 @@ hipError_t launch_tensor_absmax(const void* A, bool bf16, int64_t rows, int64_t 
 hipError_t launch_norm_quant(const void* A, bool bf16, bool layer, int64_t R, int64_t K, const float* gain,
                              const float* bias, float eps, int8_t* Q, float* scale, float* mean, float* rstd,
                              bool vec_ok, int ncu, hipStream_t st);
+// Decomposition: mask[j] = 0 for the n_o columns of largest absmax (ties to the
+// lower index), else 1; idx = those columns ascending.
+hipError_t launch_decomp_select(const float* absmax, int64_t K, int64_t n_o, int32_t* idx, float* mask,
+                                hipStream_t st);
+// out[o][r] = A[r][idx[o]] (binary32)
+hipError_t launch_decomp_gather(const void* A, bool bf16, int64_t rows, int64_t K, const int32_t* idx,
+                                int64_t n_o, float* out, int ncu, hipStream_t st);
 // out[k] = v[k] / s[k]
 hipError_t launch_fold_gain(const float* v, const float* s, int64_t K, float* out, hipStream_t st);
 
@@ -46,6 +54,12 @@ struct GemmArgs {
   void* Y;
   int out;          // OutKind
   bool vec_store;   // Y rows allow 8/16-byte stores (N % 4 == 0, aligned base)
+  // Mixed-precision decomposition (n_o > 0, float outputs only): the epilogue adds
+  // sum over o (ascending, binary32) of xo[o][t] * wo[o][n]; xo is [n_o][T] and
+  // wo is [n_o][N], both 16-byte aligned with T, N as leading dimensions.
+  const float* xo = nullptr;
+  const float* wo = nullptr;
+  int64_t n_o = 0;
 };
 
 // Prefill-shaped GEMM on the int8 MFMA units (K % 16 == 0, 16-byte aligned operands).

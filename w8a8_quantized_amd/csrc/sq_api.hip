@@ -47,10 +47,12 @@ sq_status check_gemm_args(const int8_t* Xq, const float* xs, const int8_t* Wq, c
 }
 
 sq_status run_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int64_t T,
-                   int64_t N, int64_t K, void* Y, sq_dtype y_t, hipStream_t st) {
+                   int64_t N, int64_t K, void* Y, sq_dtype y_t, hipStream_t st,
+                   const float* xo = nullptr, const float* wo = nullptr, int64_t n_o = 0) {
   sq::GemmArgs a;
   a.Xq = Xq; a.xs = xs; a.Wq = Wq; a.ws = ws;
   a.T = T; a.N = N; a.K = K; a.Y = Y;
+  a.xo = xo; a.wo = wo; a.n_o = n_o;
   a.out = y_t == SQ_F32 ? sq::kOutF32 : (y_t == SQ_BF16 ? sq::kOutBF16 : sq::kOutI32);
   a.vec_store = (N % 4 == 0) && aligned16(Y) && (y_t == SQ_I32 || aligned16(ws));
   const bool mfma_ok = (K % 16 == 0) && aligned16(Xq) && aligned16(Wq);
@@ -202,6 +204,53 @@ sq_status sq_norm_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, s
   const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
   return hip_status(sq::launch_norm_quant(X, x_t == SQ_BF16, kind == SQ_NORM_LAYER, T, K, gain, bias, eps,
                                           Xq, x_scale, mean, rstd, vec, cu_count(), stream));
+}
+
+sq_status sq_decomp_select(const float* absmax, int64_t K, int64_t n_o, int32_t* idx, float* mask,
+                           hipStream_t stream) {
+  if (!absmax || !mask || (n_o > 0 && !idx)) return SQ_ERR_NULL;
+  if (K < 1 || n_o < 0 || n_o > K) return SQ_ERR_SHAPE;
+  return hip_status(sq::launch_decomp_select(absmax, K, n_o, idx, mask, stream));
+}
+
+sq_status sq_decomp_prepare_weights(const void* W, sq_dtype w_t, int64_t N, int64_t K, const float* mask,
+                                    const int32_t* idx, int64_t n_o, int8_t* Wq, float* w_scale, float* W_out,
+                                    hipStream_t stream) {
+  if (!W || !mask || !Wq || !w_scale || (n_o > 0 && (!idx || !W_out))) return SQ_ERR_NULL;
+  if (!in_dtype(w_t)) return SQ_ERR_DTYPE;
+  if (N < 1 || K < 1 || n_o < 0 || n_o > K) return SQ_ERR_SHAPE;
+  const bool vec = (K % 8 == 0) && rows_vec16(W, K, esize(w_t)) && aligned16(Wq);
+  if (sq::launch_quant_rows(W, w_t == SQ_BF16, sq::kQuantWeights, N, K, mask, nullptr, Wq, w_scale, vec,
+                            cu_count(), stream) != hipSuccess)
+    return SQ_ERR_HIP;
+  return hip_status(sq::launch_decomp_gather(W, w_t == SQ_BF16, N, K, idx, n_o, W_out, cu_count(), stream));
+}
+
+sq_status sq_decomp_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* mask,
+                              const int32_t* idx, int64_t n_o, int8_t* Xq, float* x_scale, float* X_out,
+                              hipStream_t stream) {
+  sq_status r = check_act_args(X, x_t, T, K);
+  if (r != SQ_OK) return r;
+  if (!mask || !Xq || !x_scale || (n_o > 0 && (!idx || !X_out))) return SQ_ERR_NULL;
+  if (n_o < 0 || n_o > K) return SQ_ERR_SHAPE;
+  const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
+  // per-row range and codes of X with the outlier columns multiplied by 0
+  if (sq::launch_quant_rows(X, x_t == SQ_BF16, sq::kQuantWeights, T, K, mask, nullptr, Xq, x_scale, vec,
+                            cu_count(), stream) != hipSuccess)
+    return SQ_ERR_HIP;
+  return hip_status(sq::launch_decomp_gather(X, x_t == SQ_BF16, T, K, idx, n_o, X_out, cu_count(), stream));
+}
+
+sq_status sq_decomp_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                         const float* X_out, const float* W_out, int64_t T, int64_t N, int64_t K, int64_t n_o,
+                         void* Y, sq_dtype y_t, hipStream_t stream) {
+  sq_status r = check_gemm_args(Xq, x_scale, Wq, w_scale, T, N, K, Y, y_t);
+  if (r != SQ_OK) return r;
+  if (y_t == SQ_I32) return SQ_ERR_DTYPE;
+  if (n_o < 0 || n_o > K) return SQ_ERR_SHAPE;
+  if (n_o > 0 && (!X_out || !W_out)) return SQ_ERR_NULL;
+  if (n_o > 0 && (!aligned16(X_out) || !aligned16(W_out))) return SQ_ERR_ARG;
+  return run_gemm(Xq, x_scale, Wq, w_scale, T, N, K, Y, y_t, stream, X_out, W_out, n_o);
 }
 
 sq_status sq_w8a8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,

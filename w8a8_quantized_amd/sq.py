@@ -41,6 +41,10 @@ _SIGS = {
     "sq_quant_act_per_tensor": ([_P, _I, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "sq_fold_norm_gain": ([_P, _P, _I64, _P, _P], _I),
     "sq_norm_quant_act": ([_P, _I, _I64, _I64, _I, _P, _P, _F, _P, _P, _P, _P, _P], _I),
+    "sq_decomp_select": ([_P, _I64, _I64, _P, _P, _P], _I),
+    "sq_decomp_prepare_weights": ([_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P], _I),
+    "sq_decomp_quant_act": ([_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P], _I),
+    "sq_decomp_gemm": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_linear_workspace_size": ([_I64, _I64], _SZ),
     "sq_w8a8_linear": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
@@ -215,6 +219,59 @@ def sq_norm_quant_act(X, kind, gain, bias=None, eps=1e-6, Xq=None, x_scale=None,
                                   float(eps), _ptr(Xq), _ptr(x_scale), _ptr(mean), _ptr(rstd),
                                   _stream(X.device)))
     return Xq, x_scale, mean, rstd
+
+
+def sq_decomp_select(absmax, n_o, idx=None, mask=None):
+    """The n_o channels of largest absmax (ascending) and the 0/1 column mask."""
+    K = absmax.numel()
+    idx = _want(idx, (n_o,), torch.int32, absmax.device)
+    mask = _want(mask, (K,), torch.float32, absmax.device)
+    _check(_lib.sq_decomp_select(_ptr(absmax), K, int(n_o), _ptr(idx) if n_o else None, _ptr(mask),
+                                 _stream(absmax.device)))
+    return idx, mask
+
+
+def sq_decomp_prepare_weights(W, mask, idx, Wq=None, w_scale=None, W_out=None):
+    """Bulk int8 weights (outlier columns zeroed), w_scale, W_out [n_o, N]."""
+    N, K = W.shape
+    n_o = idx.numel()
+    Wq = _want(Wq, (N, K), torch.int8, W.device)
+    w_scale = _want(w_scale, (N,), torch.float32, W.device)
+    W_out = _want(W_out, (n_o, N), torch.float32, W.device)
+    _check(_lib.sq_decomp_prepare_weights(_ptr(W), _dt(W), N, K, _ptr(mask), _ptr(idx) if n_o else None,
+                                          n_o, _ptr(Wq), _ptr(w_scale), _ptr(W_out) if n_o else None,
+                                          _stream(W.device)))
+    return Wq, w_scale, W_out
+
+
+def sq_decomp_quant_act(X, mask, idx, Xq=None, x_scale=None, X_out=None):
+    """Bulk per-token int8 codes (outlier columns zeroed), x_scale, X_out [n_o, T]."""
+    T, K = X.shape
+    n_o = idx.numel()
+    Xq = _want(Xq, (T, K), torch.int8, X.device)
+    x_scale = _want(x_scale, (T,), torch.float32, X.device)
+    X_out = _want(X_out, (n_o, T), torch.float32, X.device)
+    _check(_lib.sq_decomp_quant_act(_ptr(X), _dt(X), T, K, _ptr(mask), _ptr(idx) if n_o else None, n_o,
+                                    _ptr(Xq), _ptr(x_scale), _ptr(X_out) if n_o else None,
+                                    _stream(X.device)))
+    return Xq, x_scale, X_out
+
+
+def sq_decomp_gemm(Xq, x_scale, Wq, w_scale, X_out, W_out, out_dtype=torch.bfloat16, Y=None):
+    """dequant(Xq @ Wq^T) + X_out^T @ W_out (binary32), fused in one launch."""
+    T, K = Xq.shape
+    N, K2 = Wq.shape
+    n_o = X_out.shape[0]
+    if K != K2 or tuple(W_out.shape) != (n_o, N) or X_out.shape[1] != T:
+        raise ValueError("shapes: Xq [T, K], Wq [N, K], X_out [n_o, T], W_out [n_o, N]")
+    yt = _DT.get(out_dtype)
+    if yt is None or out_dtype == torch.int32:
+        raise ValueError(f"out_dtype {out_dtype} not accepted")
+    Y = _want(Y, (T, N), out_dtype, Xq.device)
+    _check(_lib.sq_decomp_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale),
+                               _ptr(X_out) if n_o else None, _ptr(W_out) if n_o else None, T, N, K, n_o,
+                               _ptr(Y), yt, _stream(Xq.device)))
+    return Y
 
 
 def sq_w8a8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
