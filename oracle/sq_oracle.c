@@ -307,6 +307,123 @@ void sqo_add(const float *a, const float *b, int64_t n, float *out)
     for (int64_t i = 0; i < n; ++i) out[i] = a[i] + b[i];
 }
 
+/* FP8 variant ([P3] "A strong answer", the formats paragraph: per-token FP8
+ * E4M3 activations keep about 3 mantissa bits of relative precision whatever the
+ * token's maximum, so smoothing matters less there).  The page does not write
+ * the FP8 quantiser out; the reading used is the int8 round trip with the E4M3
+ * grid in place of the integers: scale = amax / 448 (448 is the largest finite
+ * E4M3 value), code = the E4M3 value nearest to v / scale (ties to even mantissa),
+ * saturated to +-448; an all-zero row gets scale 1 and codes 0.
+ *
+ * E4M3 (OCP FP8): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 holds the subnormals m * 2^-9; 0x7F / 0xFF are NaN (never
+ * produced).  Decoding is exact in binary32. */
+static float e4m3_value(int e, int m)
+{
+    return e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+}
+
+uint8_t sqo_e4m3_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    float a = fabsf(v);
+    if (a >= 448.0f) return sign | 0x7E;
+    /* the E4M3 neighbours below and above a, found by walking the grid */
+    int best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        float x = e4m3_value(c >> 3, c & 7);
+        if (x <= a) best = c;
+        else break;
+    }
+    float lo = e4m3_value(best >> 3, best & 7);
+    if (lo == a || best == 0x7E) return sign | (uint8_t)best;
+    int up = best + 1;
+    float hi = e4m3_value(up >> 3, up & 7);
+    double dl = (double)a - (double)lo, dh = (double)hi - (double)a;
+    int pick = dl < dh ? best : dh < dl ? up : ((best & 1) ? up : best);   /* tie: even code */
+    return sign | (uint8_t)pick;
+}
+
+float sqo_e4m3_decode(uint8_t c)
+{
+    float v = e4m3_value((c >> 3) & 15, c & 7);
+    return (c & 0x80) ? -v : v;
+}
+
+/* One row of smoothed values -> E4M3 codes and the row scale. */
+static void quantize_row_fp8(const float *v, int64_t len, uint8_t *q, float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t k = 0; k < len; ++k) {
+        float a = fabsf(v[k]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale = 1.0f;
+        for (int64_t k = 0; k < len; ++k) q[k] = 0;
+        return;
+    }
+    float sc = amax / 448.0f;
+    *scale = sc;
+    for (int64_t k = 0; k < len; ++k) q[k] = sqo_e4m3_encode(v[k] / sc);
+}
+
+/* FP8 counterparts of sqo_quantize_weights (W diag(s), per output channel) and
+ * sqo_quant_act (X diag(s)^-1, per token). */
+void sqo_quantize_weights_fp8(const float *W, int64_t N, int64_t K, const float *s,
+                              uint8_t *Wq, float *w_scale)
+{
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k)
+                row[k] = s ? W[n * K + k] * s[k] : W[n * K + k];
+            quantize_row_fp8(row, K, Wq + n * K, w_scale + n);
+        }
+        free(row);
+    }
+}
+
+void sqo_quant_act_fp8(const float *X, int64_t T, int64_t K, const float *s,
+                       uint8_t *Xq, float *x_scale)
+{
+#pragma omp parallel
+    {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t k = 0; k < K; ++k)
+                row[k] = s ? X[t * K + k] / s[k] : X[t * K + k];
+            quantize_row_fp8(row, K, Xq + t * K, x_scale + t);
+        }
+        free(row);
+    }
+}
+
+/* Exact dot products of decoded E4M3 codes at the listed (t, n) pairs: every
+ * product has at most 8 significant bits and lies in [2^-18, 448^2], so a
+ * binary64 sum of up to 2^16 of them is exact; also the sum of |products|. */
+void sqo_fp8_dot_at(const uint8_t *Xq, const uint8_t *Wq, int64_t K, const int64_t *ti,
+                    const int64_t *ni, int64_t count, double *acc, double *acc_abs)
+{
+    float lut[256];
+    for (int c = 0; c < 256; ++c) lut[c] = sqo_e4m3_decode((uint8_t)c);
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < count; ++p) {
+        const uint8_t *x = Xq + ti[p] * K, *w = Wq + ni[p] * K;
+        double sum = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double pr = (double)lut[x[k]] * (double)lut[w[k]];
+            sum += pr;
+            sa += fabs(pr);
+        }
+        acc[p] = sum;
+        acc_abs[p] = sa;
+    }
+}
+
 /* Integer matmul.  [P5] "Which scales factor out": acc_tn = sum_k P_tk Q_nk.
  * Accumulated in int64; returns 1 if any sum does not fit int32, else 0. */
 int sqo_int_gemm(const int8_t *Xq, const int8_t *Wq, int64_t T, int64_t N, int64_t K,

@@ -36,7 +36,8 @@ __all__ = ["build", "col_absmax", "smooth_scales", "quantize_weights", "quant_ac
            "widen_bf16", "set_threads", "act_tensor_absmax", "quant_act_static",
            "quant_act_per_tensor", "fold_gain", "norm_stats", "norm_apply", "norm_quant_act",
            "decomp_select", "decomp_split", "decomp_outlier_product", "decomp_prepare",
-           "decomp_linear", "decomp_relative_error"]
+           "decomp_linear", "decomp_relative_error", "e4m3_encode", "e4m3_decode",
+           "quantize_weights_fp8", "quant_act_fp8", "fp8_dot_at", "fp8_relative_error"]
 
 GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
              "-std=c11", "-Wall"]
@@ -86,6 +87,15 @@ def _load():
             lib.sqo_decomp_outlier_product.argtypes = [P, P, I64, I64, I64, P]
             lib.sqo_add.argtypes = [P, P, I64, P]
             for f in ("sqo_decomp_select", "sqo_decomp_split", "sqo_decomp_outlier_product", "sqo_add"):
+                getattr(lib, f).restype = None
+            lib.sqo_e4m3_encode.argtypes = [F]
+            lib.sqo_e4m3_encode.restype = ctypes.c_uint8
+            lib.sqo_e4m3_decode.argtypes = [ctypes.c_uint8]
+            lib.sqo_e4m3_decode.restype = F
+            lib.sqo_quantize_weights_fp8.argtypes = [P, I64, I64, P, P, P]
+            lib.sqo_quant_act_fp8.argtypes = [P, I64, I64, P, P, P]
+            lib.sqo_fp8_dot_at.argtypes = [P, P, I64, P, P, I64, P, P]
+            for f in ("sqo_quantize_weights_fp8", "sqo_quant_act_fp8", "sqo_fp8_dot_at"):
                 getattr(lib, f).restype = None
             for f in ("sqo_col_absmax", "sqo_smooth_scales", "sqo_quantize_weights",
                       "sqo_quant_act", "sqo_dequant", "sqo_dequant_at", "sqo_to_bf16"):
@@ -308,6 +318,79 @@ def decomp_relative_error(X, W, idx):
     y, *_ = decomp_linear(X, idx, Wq, ws, Wo)
     Y = exact_product(X, W)
     return float(np.linalg.norm(y.astype(np.float64) - Y) / np.linalg.norm(Y))
+
+
+def e4m3_encode(v):
+    """[P3] formats paragraph, FP8 E4M3: nearest E4M3 code (ties to the even
+    code), saturated at +-448; elementwise over an array."""
+    v = np.asarray(v, np.float32)
+    lib = _load()
+    out = np.array([lib.sqo_e4m3_encode(float(x)) for x in v.ravel()], np.uint8)
+    return out.reshape(v.shape)
+
+
+def e4m3_decode(c):
+    """E4M3 code -> binary32 value (exact)."""
+    c = np.asarray(c, np.uint8)
+    lib = _load()
+    lut = np.array([lib.sqo_e4m3_decode(i) for i in range(256)], np.float32)
+    return lut[c]
+
+
+def quantize_weights_fp8(W, s=None):
+    """FP8 E4M3 per-output-channel codes of W diag(s): scale = row amax / 448.
+    Returns (Wq uint8 [N,K] E4M3 codes, w_scale float32 [N])."""
+    W = _f32(W)
+    N, K = W.shape
+    s = None if s is None else _f32(s)
+    Wq = np.empty((N, K), np.uint8)
+    ws = np.empty(N, np.float32)
+    _load().sqo_quantize_weights_fp8(_ptr(W), N, K, _ptr(s), _ptr(Wq), _ptr(ws))
+    return Wq, ws
+
+
+def quant_act_fp8(X, s=None):
+    """FP8 E4M3 per-token codes of X diag(s)^-1.  Returns (Xq uint8, x_scale)."""
+    X = _f32(X)
+    T, K = X.shape
+    s = None if s is None else _f32(s)
+    Xq = np.empty((T, K), np.uint8)
+    xs = np.empty(T, np.float32)
+    _load().sqo_quant_act_fp8(_ptr(X), T, K, _ptr(s), _ptr(Xq), _ptr(xs))
+    return Xq, xs
+
+
+def fp8_dot_at(Xq, Wq, ti, ni):
+    """Exact (binary64) dot products of decoded codes at (t, n) pairs, and the
+    sums of |products|."""
+    Xq = np.ascontiguousarray(Xq, np.uint8)
+    Wq = np.ascontiguousarray(Wq, np.uint8)
+    ti = np.ascontiguousarray(ti, np.int64)
+    ni = np.ascontiguousarray(ni, np.int64)
+    assert Xq.shape[1] == Wq.shape[1] and ti.shape == ni.shape
+    acc = np.empty(ti.size, np.float64)
+    sab = np.empty(ti.size, np.float64)
+    _load().sqo_fp8_dot_at(_ptr(Xq), _ptr(Wq), Xq.shape[1], _ptr(ti), _ptr(ni), ti.size, _ptr(acc),
+                           _ptr(sab))
+    return acc, sab
+
+
+def fp8_relative_error(X, W, alpha):
+    """[P3]: relative Frobenius error of the layer with FP8 E4M3 per-token
+    activations and per-output-channel weights (exact accumulation, binary32
+    epilogue); alpha=None: no smoothing."""
+    X32, W32 = _f32(X), _f32(W)
+    if alpha is None:
+        s = None
+    else:
+        s = smooth_scales(col_absmax(X32), col_absmax(W32), alpha)
+    Wq, ws = quantize_weights_fp8(W32, s)
+    Xq, xs = quant_act_fp8(X32, s)
+    lut = e4m3_decode(np.arange(256)).astype(np.float64)
+    acc = lut[Xq] @ lut[Wq].T
+    y = (acc.astype(np.float32) * (xs[:, None] * ws[None, :])).astype(np.float64)
+    Y = exact_product(X, W)
+    return float(np.linalg.norm(y - Y) / np.linalg.norm(Y))
 
 
 def int_gemm(Xq, Wq):
