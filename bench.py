@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W8A8 linear TOPS incl. per-token quant (prefill); HBM GB/s (quant, decode GEMM)"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 
 
 def _gemm_bytes(T, N, K, out_bytes):
@@ -311,7 +312,12 @@ def main():
     m_buf, r_buf = torch.empty(T, device=dev), torch.empty(T, device=dev)
     t_norm = batched(lambda x_: sq.sq_norm_quant_act(x_, "rms", gfold, Xq=Xq, x_scale=xs, mean=m_buf,
                                                      rstd=r_buf), Xc)
-    del Wc, Xc
+    # FP8 E4M3 variant of the same layer: quantisers and the FP8 matrix-core GEMM
+    Wq8, ws8 = sq.sq_quantize_weights_fp8(W, s)
+    Xq8, xs8 = sq.sq_quant_act_fp8(X, s)
+    t_q8 = batched(lambda x_: sq.sq_quant_act_fp8(x_, s, Xq=Xq8, x_scale=xs8), Xc)
+    t_g8 = batched(lambda _: sq.sq_fp8_gemm(Xq8, xs8, Wq8, ws8, out_dtype=ydt, Y=Y), [None])
+    del Wc, Xc, Wq8, Xq8
     ops = 2.0 * T * N * K
     ob = 2 if ydt == torch.bfloat16 else 4
     ib = 2 if xdt == torch.bfloat16 else 4
@@ -347,6 +353,10 @@ def main():
             "note": "bytes are algorithmic; the dynamic per-tensor quantiser reads X twice "
                     "(range, then codes)"},
         "norm_quant_act_rms": _rate(ib * T * K + 4 * K + T * K + 4 * T + 8 * T, t_norm),
+        "fp8": {"quant_act": _rate(qbytes, t_q8), "gemm_us": t_g8 * 1e3,
+                "gemm_TFLOP/s": ops / (t_g8 * 1e-3) / 1e12,
+                "gemm_frac_fp8_peak": ops / (t_g8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                "linear_TFLOP/s": ops / ((t_q8 + t_g8) * 1e-3) / 1e12},
     }
     if not args.no_decode:
         del X, Xs, W, Wq, Xq, Y

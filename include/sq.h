@@ -303,6 +303,36 @@ sq_status sq_decomp_gemm(const int8_t *Xq, const float *x_scale, const int8_t *W
                          hipStream_t stream);
 
 /*
+ * FP8 E4M3 variant (inferenceinterviews page, "A strong answer", formats
+ * paragraph: per-token FP8 activations keep about 3 mantissa bits whatever the
+ * token's maximum).  The quantiser is the int8 one with the E4M3 grid:
+ *     scale = amax / 448 (binary32), code = the E4M3 value nearest to v / scale
+ *     (ties to the even code), saturated at +-448; scale 1 and codes 0 for a
+ *     zero row.  E4M3 is the OCP format: bias 7, 3 mantissa bits, exponent
+ *     field 0 for the subnormals m * 2^-9; codes 0x7F / 0xFF (NaN) never occur.
+ * sq_quantize_weights_fp8: per output channel of W diag(s) (as sq_quantize_weights);
+ * sq_quant_act_fp8: per token of X diag(s)^-1 (as sq_quant_act).
+ *   Wq / Xq  device uint8 [N][K] / [T][K] of E4M3 codes, written
+ */
+sq_status sq_quantize_weights_fp8(const void *W, sq_dtype w_t, int64_t N, int64_t K,
+                                  const float *s, uint8_t *Wq, float *w_scale, hipStream_t stream);
+sq_status sq_quant_act_fp8(const void *X, sq_dtype x_t, int64_t T, int64_t K, const float *s,
+                           uint8_t *Xq, float *x_scale, hipStream_t stream);
+
+/*
+ * FP8 GEMM:  acc[t][n] = sum_k e4m3(Xq[t][k]) * e4m3(Wq[n][k]),
+ *            Y[t][n]   = fl32(acc * fl32(x_scale[t] * w_scale[n]))   (then bf16 RNE)
+ * on the FP8 matrix cores (binary32 accumulation).  Every product of two E4M3
+ * values is exact, but the hardware sums them at less than full binary32
+ * precision when their magnitudes differ widely, so acc is not the exact sum:
+ * it is within 2^-10 * sum_k |products| of it (a measured property of the
+ * instruction; the exact sum is the reference).  y_t = SQ_F32 or SQ_BF16.
+ */
+sq_status sq_fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *Wq,
+                      const float *w_scale, int64_t T, int64_t N, int64_t K, void *Y,
+                      sq_dtype y_t, hipStream_t stream);
+
+/*
  * W8A8 GEMM with int32 accumulation and the dequantising epilogue
  * (mercemay.com "Activation Outlier Channels and Mixed-Precision Decomposition",
  * section "Decomposition": integer matmul, float epilogue multiplying by the

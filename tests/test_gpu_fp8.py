@@ -1,0 +1,138 @@
+"""Parity of the FP8 E4M3 variant (sq_quantize_weights_fp8, sq_quant_act_fp8,
+sq_fp8_gemm) with the CPU oracle, through the C ABI.
+
+Bar: E4M3 codes and scales bit-exact.  The GEMM accumulates exact E4M3 products
+on the matrix cores at less than full binary32 precision, so its accumulators are
+compared with the oracle's exact (binary64) dot products within
+2^-10 * sum_k |products|; outputs within that bound times x_scale * w_scale plus
+one binary32 rounding (and the bf16 rounding, 2^-8 relative, for bf16 out).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import DEV, dev_act, host, misaligned
+
+pytestmark = pytest.mark.gpu
+ACC_BOUND = 2.0 ** -10
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import w8a8_quantized_amd as m   # raises if libsq.so is missing: no fallback
+    assert torch.cuda.is_available()
+    return m
+
+
+def _case(seed, T, K, N, dtype):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    if K > 4:
+        X[:, rng.choice(K, 3, replace=False)] *= 40
+    if dtype == "bf16":
+        X = torch.from_numpy(X).to(torch.bfloat16).float().numpy()
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    s = rng.uniform(0.3, 4.0, K).astype(np.float32)
+    return X, W, s
+
+
+SHAPES = [(1, 8, 16), (16, 300, 512), (70, 200, 1040), (300, 520, 2048), (33, 64, 133), (257, 264, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,N,K", SHAPES)
+def test_fp8_quantisers(sq, dtype, T, N, K):
+    X, W, s = _case(T + N + K, T, K, N, dtype)
+    sd = torch.from_numpy(s).to(DEV)
+    Xd = dev_act(X, dtype)
+    Xq, xs = sq.sq_quant_act_fp8(Xd, sd)
+    Xq_r, xs_r = O.quant_act_fp8(X, s)
+    assert np.array_equal(host(xs), xs_r) and np.array_equal(host(Xq), Xq_r)
+    Wr = torch.from_numpy(W).to(torch.bfloat16).float().numpy() if dtype == "bf16" else W
+    Wd = dev_act(Wr, dtype)
+    Wq, ws = sq.sq_quantize_weights_fp8(Wd, sd)
+    Wq_r, ws_r = O.quantize_weights_fp8(Wr, s)
+    assert np.array_equal(host(ws), ws_r) and np.array_equal(host(Wq), Wq_r)
+    if T * K > 16:
+        Xq2, xs2 = sq.sq_quant_act_fp8(misaligned(Xd), sd)
+        assert np.array_equal(host(Xq2), Xq_r) and np.array_equal(host(xs2), xs_r)
+
+
+def test_fp8_quantiser_zero_and_saturation(sq):
+    X = np.zeros((3, 64), np.float32)
+    X[1, 5] = -7.0
+    X[2] = np.linspace(-3, 3, 64, dtype=np.float32)
+    Xq, xs = sq.sq_quant_act_fp8(dev_act(X, "f32"))
+    Xq_r, xs_r = O.quant_act_fp8(X, None)
+    assert np.array_equal(host(Xq), Xq_r) and np.array_equal(host(xs), xs_r)
+    assert host(xs)[0] == 1.0 and not host(Xq)[0].any() and host(Xq)[1, 5] == 0xFE
+
+
+def _check_gemm(sq, Xq_r, xs_r, Wq_r, ws_r, ti=None, ni=None):
+    T, N = Xq_r.shape[0], Wq_r.shape[0]
+    Xq = torch.from_numpy(Xq_r).to(DEV)
+    Wq = torch.from_numpy(Wq_r).to(DEV)
+    ones_t, ones_n = torch.ones(T, device=DEV), torch.ones(N, device=DEV)
+    acc = host(sq.sq_fp8_gemm(Xq, ones_t, Wq, ones_n, out_dtype=torch.float32))
+    y32 = host(sq.sq_fp8_gemm(Xq, torch.from_numpy(xs_r).to(DEV), Wq, torch.from_numpy(ws_r).to(DEV),
+                              out_dtype=torch.float32))
+    yb = host(sq.sq_fp8_gemm(Xq, torch.from_numpy(xs_r).to(DEV), Wq, torch.from_numpy(ws_r).to(DEV),
+                             out_dtype=torch.bfloat16))
+    if ti is None:
+        ti, ni = np.repeat(np.arange(T), N), np.tile(np.arange(N), T)
+    exact, sab = O.fp8_dot_at(Xq_r, Wq_r, ti, ni)
+    g = acc[ti, ni].astype(np.float64)
+    ratio = np.abs(g - exact) / np.maximum(sab, 1e-300)
+    assert np.all(np.abs(g - exact) <= ACC_BOUND * sab), ratio.max()
+    sc = (xs_r[ti] * ws_r[ni]).astype(np.float32).astype(np.float64)
+    y_exact = exact * sc
+    tol = ACC_BOUND * sab * sc + 2.0 ** -23 * np.abs(y_exact) + 1e-37
+    assert np.all(np.abs(y32[ti, ni] - y_exact) <= tol)
+    ybf = O.widen_bf16(yb[ti, ni]).astype(np.float64)
+    assert np.all(np.abs(ybf - y_exact) <= tol + 2.0 ** -8 * np.abs(y_exact))
+    return float(ratio.max())
+
+
+@pytest.mark.parametrize("T,N,K", SHAPES)
+def test_fp8_gemm_accuracy(sq, T, N, K):
+    X, W, s = _case(3 * T + N + K, T, K, N, "f32")
+    Xq_r, xs_r = O.quant_act_fp8(X, s)
+    Wq_r, ws_r = O.quantize_weights_fp8(W, s)
+    r = _check_gemm(sq, Xq_r, xs_r, Wq_r, ws_r)
+    print(f"fp8 gemm {T}x{N}x{K}: max |acc - exact| / sum|p| = {r:.3g}")
+
+
+def test_fp8_gemm_misaligned_generic(sq):
+    X, W, s = _case(9, 20, 64, 36, "f32")
+    Xq_r, xs_r = O.quant_act_fp8(X, s)
+    Wq_r, ws_r = O.quantize_weights_fp8(W, s)
+    Xq = misaligned(torch.from_numpy(Xq_r).to(DEV))
+    Wq = misaligned(torch.from_numpy(Wq_r).to(DEV))
+    y = host(sq.sq_fp8_gemm(Xq, torch.from_numpy(xs_r).to(DEV), Wq, torch.from_numpy(ws_r).to(DEV),
+                            out_dtype=torch.float32))
+    ti, ni = np.repeat(np.arange(20), 36), np.tile(np.arange(36), 20)
+    exact, sab = O.fp8_dot_at(Xq_r, Wq_r, ti, ni)
+    sc = (xs_r[ti] * ws_r[ni]).astype(np.float32).astype(np.float64)
+    assert np.all(np.abs(y[ti, ni] - exact * sc) <= 64 * 2.0 ** -24 * sab * sc + 2.0 ** -23 * np.abs(exact * sc))
+
+
+@pytest.mark.parametrize("name", ["heavy_t8192_k8192_n8192", "prefill_t2048_k4096_n16384"])
+def test_fp8_full_size(sq, name):
+    """The workload's smoothed operands in FP8: all codes and scales; the GEMM on
+    sampled (t, n) pairs against exact dot products."""
+    w = WL.make(name)
+    Xs = w.X if w.X_calib is None else w.X_calib
+    s = O.smooth_scales(O.col_absmax(Xs), O.col_absmax(w.W), w.alpha)
+    sd = torch.from_numpy(s).to(DEV)
+    Xq, xs = sq.sq_quant_act_fp8(dev_act(w.X, w.x_dtype), sd)
+    Wq, ws = sq.sq_quantize_weights_fp8(torch.from_numpy(w.W).to(DEV), sd)
+    Xq_r, xs_r = O.quant_act_fp8(w.X, s)
+    Wq_r, ws_r = O.quantize_weights_fp8(w.W, s)
+    assert np.array_equal(host(xs), xs_r) and np.array_equal(host(Xq), Xq_r)
+    assert np.array_equal(host(ws), ws_r) and np.array_equal(host(Wq), Wq_r)
+    rng = np.random.default_rng(8)
+    ti, ni = rng.integers(0, w.T, 50_000), rng.integers(0, w.N, 50_000)
+    r = _check_gemm(sq, Xq_r, xs_r, Wq_r, ws_r, ti, ni)
+    print(f"fp8 gemm {name}: max |acc - exact| / sum|p| = {r:.3g}")

@@ -7,6 +7,7 @@ and fails if it has not been built.
 from .sq import (SQ_BF16, SQ_F32, SQ_I32, SQ_MAX_K, EXPORTED, LIB_PATH,  # noqa: F401
                  SQ_NORM_LAYER, SQ_NORM_RMS, sq_fold_norm_gain, sq_norm_quant_act,
                  sq_decomp_gemm, sq_decomp_prepare_weights, sq_decomp_quant_act, sq_decomp_select,
+                 sq_fp8_gemm, sq_quant_act_fp8, sq_quantize_weights_fp8,
                  sq_act_absmax, sq_col_absmax, sq_quant_act, sq_quant_act_per_tensor,
                  sq_quant_act_static, sq_quantize_weights, sq_smooth_scales,
                  sq_smooth_scales_from_absmax, sq_status_string, sq_w8a8_gemm, sq_w8a8_linear,

@@ -6,9 +6,12 @@
 namespace sq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kQmax = 127;   // symmetric int8 grid [-127, 127]
+constexpr float kF8max = 448.0f;   // largest finite FP8 E4M3 value
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
@@ -45,12 +48,48 @@ __device__ __forceinline__ int quant_code(float v, double rscale) {
 // 1.5 * 2^23 rounds it to an integer, ties to even, in the binary32 add itself;
 // the low byte of the sum's bit pattern is that integer in two's complement.
 __device__ __forceinline__ uint32_t quant_code_bits(float v, double rscale) {
-  float q = div_by_recip(v, rscale);
-  q = __builtin_fminf(__builtin_fmaxf(q, -(float)kQmax), (float)kQmax);
+  const float q = __builtin_amdgcn_fmed3f(div_by_recip(v, rscale), -(float)kQmax, (float)kQmax);
   return __float_as_uint(q + 12582912.0f);
 }
 
-// Low bytes of four words -> one word (byte i from word i).
+// FP8 E4M3 (OCP: bias 7, 3 mantissa bits, exponent field 0 = subnormals m * 2^-9,
+// largest finite 448) code of the binary32 value q: nearest E4M3 value, ties to
+// the even code, saturated at +-448; the sign of q is kept (-0 -> 0x80).
+//   |q| < 2^-6: the subnormal grid has step 2^-9, so the code is rne(|q| * 512)
+//               (0..8; 8 is the smallest normal, code 0x08);
+//   otherwise:  rounding the binary32 mantissa to 3 bits (ties to even, a carry
+//               moves into the exponent) and re-biasing the exponent from 127 to 7.
+__host__ __device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 24) & 0x80u;
+  const float a = __builtin_fminf(__builtin_fabsf(q), 448.0f);
+  if (a < 0.015625f) {
+    const float m = (a * 512.0f + 12582912.0f) - 12582912.0f;   // exact scaling, then rne
+    return sign | (uint32_t)m;
+  }
+  uint32_t b = __builtin_bit_cast(uint32_t, a);
+  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+  return sign | (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+}
+
+// Four E4M3 codes (byte i from q[i]) by the hardware conversion, on inputs
+// clamped to +-448 first.  On clamped inputs it rounds exactly as e4m3_code
+// (checked on the GPU on every binary32 value in [-448, 448] with its top 20 bits
+// varied and 5 low-bit patterns, subnormal results and signed zeros included).
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
+  auto c = [](float q) { return __builtin_amdgcn_fmed3f(q, -kF8max, kF8max); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c(q0), c(q1), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c(q2), c(q3), lo, true);
+}
+
+// Binary32 value of an E4M3 code (exact).
+__host__ __device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e == 0 ? (float)m * 0.001953125f                       // m * 2^-9
+                         : __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+// Low bytes of four words -> one word (byte i from word i).// Low bytes of four words -> one word (byte i from word i).
 __device__ __forceinline__ uint32_t pack4_lowbytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
   const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);

@@ -19,6 +19,8 @@
 // conflicts.  Workgroups are remapped so that each XCD (which owns a private L2)
 // works through a contiguous run of tiles, grouped 8 output-channel tiles wide,
 // which keeps the operand panels it streams shared inside that L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,10 +35,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // Four consecutive outputs of one row.  VEC: one 8/16-byte store (the caller
 // guarantees all four exist: N % 4 == 0 and the first is in range); otherwise
 // element stores of the nrem (>= 1) outputs that exist.
-template <int OUT, bool VEC>
-__device__ __forceinline__ void store4(void* Y, int64_t off, int nrem, const int* a, float sc_t,
+template <int OUT, bool VEC, typename A>
+__device__ __forceinline__ void store4(void* Y, int64_t off, int nrem, const A* a, float sc_t,
                                        const float* wsv) {
-  if (OUT == kOutI32) {
+  if constexpr (OUT == kOutI32) {
     int* y = static_cast<int*>(Y) + off;
     if (VEC) { *reinterpret_cast<int4*>(y) = make_int4(a[0], a[1], a[2], a[3]); return; }
     for (int e = 0; e < 4 && e < nrem; ++e) y[e] = a[e];
@@ -93,8 +95,8 @@ __device__ __forceinline__ void outlier_sum4(const float* __restrict__ x, int64_
 
 // Element stores of the nrem (>= 1) outputs that exist, each the dequantised
 // value plus its outlier-channel product (float outputs only).
-template <int OUT>
-__device__ __forceinline__ void store4o(void* Y, int64_t off, int nrem, const int* a, float sc_t,
+template <int OUT, typename A>
+__device__ __forceinline__ void store4o(void* Y, int64_t off, int nrem, const A* a, float sc_t,
                                         const float* wsv, const float* so) {
   for (int e = 0; e < 4 && e < nrem; ++e) {
     const float v = (float)a[e] * (sc_t * wsv[e]) + so[e];
@@ -142,7 +144,14 @@ constexpr int kLgkm0 = ~0x0F00;
 // and Mixed-Precision Decomposition", section "Decomposition"): the float
 // epilogue value gets the binary32 product of the outlier channels added,
 //   y = fl32(fl32(acc) * fl32(xs * ws)) + (sum over o ascending of xo[o][t] * wo[o][n]).
-template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC, bool OUTL>
+//
+// F8 (FP8 E4M3 operands, inferenceinterviews.com formats paragraph): the same
+// byte tiles feed v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) with
+// binary32 accumulators.  One MFMA takes, per lane, the two 16-byte chunks that
+// two consecutive int8 k-steps would take, for A and B alike, so every product
+// pairs the same k.  Fragments are read straight into the 8-register operands,
+// one step at a time (the 16-wave tile has no registers for a second set).
+template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC, bool OUTL, bool F8>
 __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy,
@@ -218,11 +227,14 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) cofs[kk] = ((kk * 2 + fc) ^ sw) * 16;
 
-  v16i acc[RN][RT];
+  using AccT = std::conditional_t<F8, v16f, v16i>;
+  using AccE = std::conditional_t<F8, float, int>;
+  static_assert(!F8 || OUT != kOutI32, "FP8 accumulators are binary32");
+  AccT acc[RN][RT];
 #pragma unroll
   for (int i = 0; i < RN; ++i)
 #pragma unroll
-    for (int j = 0; j < RT; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < RT; ++j) acc[i][j] = AccT{};
 
   v4i fa[2][RN], fb[2][RT];
   auto read_frags = [&](int slot, const int8_t* L, int kk) {
@@ -232,11 +244,35 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     for (int j = 0; j < RT; ++j) fb[slot][j] = *reinterpret_cast<const v4i*>(L + b_base + cofs[kk] + j * 32 * BK);
   };
   auto mfmas = [&](int slot, int first, int count) {
+    if constexpr (!F8) {
 #pragma unroll
-    for (int q = 0; q < RN * RT; ++q) {
-      if (q < first || q >= first + count) continue;
-      const int i = q / RT, j = q % RT;
-      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+      for (int q = 0; q < RN * RT; ++q) {
+        if (q < first || q >= first + count) continue;
+        const int i = q / RT, j = q % RT;
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  // FP8: fragments of one 64-deep step (the chunks of int8 k-steps 2q and
+  // 2q + 1, read straight into the 8-register operands), then its MFMAs
+  auto step8 = [&](const int8_t* L, int q) {
+    if constexpr (F8) {
+      v8i a8[RN], b8[RT];
+#pragma unroll
+      for (int i = 0; i < RN; ++i)
+        a8[i] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(L + a_base + cofs[2 * q] + i * 32 * BK),
+                                        *reinterpret_cast<const v4i*>(L + a_base + cofs[2 * q + 1] + i * 32 * BK),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+        b8[j] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(L + b_base + cofs[2 * q] + j * 32 * BK),
+                                        *reinterpret_cast<const v4i*>(L + b_base + cofs[2 * q + 1] + j * 32 * BK),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int i = 0; i < RN; ++i)
+#pragma unroll
+        for (int j = 0; j < RT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8[i], b8[j], acc[i][j], 0, 0, 0, 127, 0, 127);
     }
   };
   // wait until at most `later` stages of this wave's DMA loads are in flight
@@ -265,6 +301,20 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     if (s < nst) issue(s, s * BK);
   wait_vm(nst - 1 < STAGES - 1 ? nst - 1 : STAGES - 1);
   bar();
+
+  if constexpr (F8) {
+    for (int s = 0; s < nst; ++s) {
+      const int8_t* L = lds + (s % STAGES) * STAGE_BYTES;
+#pragma unroll
+      for (int q = 0; q < KK / 2; ++q) step8(L, q);
+      if (s + 1 < nst) {
+        const int later = nst - 2 - s < STAGES - 2 ? nst - 2 - s : STAGES - 2;
+        wait_vm_lds(later);
+        bar();
+        if (s + STAGES < nst) issue(s % STAGES, (s + STAGES) * BK);
+      }
+    }
+  } else {
   read_frags(0, lds, 0);
 
   for (int s = 0; s < nst; ++s) {
@@ -299,6 +349,7 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
   }
 
   if (VEC) {
@@ -340,7 +391,7 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             int8_t* dst = E + fr * ROWB + ((i - ib) * 32 + 8 * g + 4 * fc) * OB;
-            if (OUT == kOutI32) {
+            if constexpr (OUT == kOutI32) {
               *reinterpret_cast<v4i*>(dst) =
                   v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
             } else {
@@ -394,7 +445,7 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
         for (int g = 0; g < 4; ++g) {
           const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
           if (n >= N) continue;
-          const int a4[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          const AccE a4[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           float wsv[4] = {0.f, 0.f, 0.f, 0.f};
           if (OUT != kOutI32)
             for (int e = 0; e < 4; ++e) wsv[e] = (n + e < N) ? ws[n + e] : 0.0f;
@@ -416,29 +467,35 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
 #endif
 }
 
-template <int BN, int BT, int BK, int WN, int WT, int ST, bool VEC>
+template <int BN, int BT, int BK, int WN, int WT, int ST, bool VEC, bool F8>
 static void launch_out(int out, bool outl, dim3 grid, dim3 block, hipStream_t st, const int8_t* Xq,
                        const float* xs, const int8_t* Wq, const float* ws, int T, int N, int K, void* Y,
                        int64_t ldy, int tiles_n, int tiles_t, const float* xo, int64_t ldxo, const float* wo,
                        int64_t ldwo, int n_o) {
-#define SQ_GEMM_LAUNCH(O, L)                                                                                  \
-  hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, O, VEC, L>), grid, block, 0, st, Xq, xs, Wq, \
+#define SQ_GEMM_LAUNCH(O, L, F)                                                                                  \
+  hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, O, VEC, L, F>), grid, block, 0, st, Xq, xs, Wq, \
                      ws, T, N, K, Y, ldy, tiles_n, tiles_t, xo, ldxo, wo, ldwo, n_o)
+  if constexpr (F8) {   // FP8 operands: float outputs, no outlier term
+    if (out == kOutF32) SQ_GEMM_LAUNCH(kOutF32, false, true);
+    else SQ_GEMM_LAUNCH(kOutBF16, false, true);
+    return;
+  } else {
   switch (out) {
     case kOutF32:
-      if (outl) SQ_GEMM_LAUNCH(kOutF32, true); else SQ_GEMM_LAUNCH(kOutF32, false);
+      if (outl) SQ_GEMM_LAUNCH(kOutF32, true, false); else SQ_GEMM_LAUNCH(kOutF32, false, false);
       break;
     case kOutBF16:
-      if (outl) SQ_GEMM_LAUNCH(kOutBF16, true); else SQ_GEMM_LAUNCH(kOutBF16, false);
+      if (outl) SQ_GEMM_LAUNCH(kOutBF16, true, false); else SQ_GEMM_LAUNCH(kOutBF16, false, false);
       break;
     default:
-      SQ_GEMM_LAUNCH(kOutI32, false);
+      SQ_GEMM_LAUNCH(kOutI32, false, false);
       break;
+  }
   }
 #undef SQ_GEMM_LAUNCH
 }
 
-template <int BN, int BT, int BK, int WN, int WT, int ST>
+template <int BN, int BT, int BK, int WN, int WT, int ST, bool F8 = false>
 static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
   // Split so that every operand slice handed to one launch spans < 2^31 bytes
   // (32-bit buffer offsets), counting one tile of overhang past the edge.
@@ -456,7 +513,7 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
       const int8_t* Wq = a.Wq + nb * a.K;
       const float* xs = a.xs ? a.xs + tb : nullptr;
       const float* ws = a.ws ? a.ws + nb : nullptr;
-      const bool outl = a.n_o > 0 && a.out != kOutI32;
+      const bool outl = a.n_o > 0 && a.out != kOutI32 && !a.f8;
       const float* xo = outl ? a.xo + tb : nullptr;
       const float* wo = outl ? a.wo + nb : nullptr;
       void* Y = static_cast<char*>(a.Y) + (tb * a.N + nb) * osz;
@@ -466,9 +523,9 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
       const int per16 = a.out == kOutBF16 ? 8 : 4;
       const bool vs = a.vec_store && a.N % per16 == 0 && nb % per16 == 0;
       const int K = (int)a.K;
-      if (vs) launch_out<BN, BT, BK, WN, WT, ST, true>(a.out, outl, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N,
+      if (vs) launch_out<BN, BT, BK, WN, WT, ST, true, F8>(a.out, outl, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N,
                                                         tiles_n, tiles_t, xo, a.T, wo, a.N, (int)a.n_o);
-      else launch_out<BN, BT, BK, WN, WT, ST, false>(a.out, outl, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N,
+      else launch_out<BN, BT, BK, WN, WT, ST, false, F8>(a.out, outl, grid, block, st, Xq, xs, Wq, ws, T, N, K, Y, a.N,
                                                      tiles_n, tiles_t, xo, a.T, wo, a.N, (int)a.n_o);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -478,6 +535,13 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
+  if (a.f8) {
+    // 8 waves of 64 x 128: the FP8 step needs ~170 registers per wave, more
+    // than the 16-wave tile allows
+    const int64_t big8 = ((a.N + 255) / 256) * ((a.T + 255) / 256);
+    if (big8 >= ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true>(a, st);
+    return gemm_cfg<128, 128, 128, 2, 2, 2, true>(a, st);
+  }
   // 256x256 tiles when they fill the chip at least once, else 128x128.  The big
   // tile runs 16 waves of 64x64 (4 per SIMD): with fewer, larger wave tiles the
   // per-stage barrier and LDS latency are not covered (measured ~8% slower).
@@ -518,7 +582,40 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const int8_t* __restr
   }
 }
 
+// FP8 codes, any shape and alignment: binary32 sum over k of the decoded
+// products, then y = fl32(acc * fl32(xs * ws)).
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_fp8_generic_kernel(const uint8_t* __restrict__ Xq,
+                                                               const float* __restrict__ xs,
+                                                               const uint8_t* __restrict__ Wq,
+                                                               const float* __restrict__ ws, int64_t T,
+                                                               int64_t N, int64_t K, void* __restrict__ Y) {
+  const int64_t total = T * N;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = o / N, n = o - t * N;
+    const uint8_t* x = Xq + t * K;
+    const uint8_t* w = Wq + n * K;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) acc = acc + e4m3_value(x[k]) * e4m3_value(w[k]);
+    const float v = acc * (xs[t] * ws[n]);
+    if (OUT == kOutF32) static_cast<float*>(Y)[o] = v;
+    else static_cast<uint16_t*>(Y)[o] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
 hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st) {
+  if (a.f8) {
+    int64_t g = (a.T * a.N + 255) / 256;
+    if (g > 65536) g = 65536;
+    const uint8_t* xq = reinterpret_cast<const uint8_t*>(a.Xq);
+    const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.Wq);
+    if (a.out == kOutF32)
+      hipLaunchKernelGGL(gemm_fp8_generic_kernel<kOutF32>, dim3((unsigned)g), dim3(256), 0, st, xq, a.xs, wq, a.ws, a.T, a.N, a.K, a.Y);
+    else
+      hipLaunchKernelGGL(gemm_fp8_generic_kernel<kOutBF16>, dim3((unsigned)g), dim3(256), 0, st, xq, a.xs, wq, a.ws, a.T, a.N, a.K, a.Y);
+    return hipGetLastError();
+  }
   int64_t total = a.T * a.N;
   int64_t g = (total + 255) / 256;
   if (g > 65536) g = 65536;

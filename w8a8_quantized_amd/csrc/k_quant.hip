@@ -27,6 +27,10 @@
 // operations", quantize_dequantize with its clip argument; clip = 0 gives scale 1
 // and codes 0).
 //
+// FP8 mode (F8): the same round trip on the E4M3 grid (inferenceinterviews.com,
+// formats paragraph: per-token FP8 activations): scale = amax / 448, code = the
+// E4M3 value nearest to v / scale (ties to even), saturated at +-448.
+//
 // Slow path (any shape/alignment): one workgroup per row, two passes over the
 // row with plain IEEE binary32 divisions; identical results.
 #include "common.h"
@@ -78,7 +82,8 @@ __device__ __forceinline__ void static_scale(const float* clip, float& scale, do
 // MODE: 0 = activations, per-row range (divide by s); 1 = weights, per-row range
 // (multiply by s); 2 = activations, given range *clip (divide by s).
 // FULL: K == CPT * 2048, every thread's chunks exist (no per-chunk masks).
-template <typename T, int MODE, bool HAS_S, int CPT, bool FULL>
+// F8: E4M3 codes (MODE 0 or 1) instead of int8.
+template <typename T, int MODE, bool HAS_S, int CPT, bool FULL, bool F8>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A, int64_t R,
                                                          int64_t K, const float* __restrict__ s,
                                                          const float* __restrict__ clip,
@@ -133,8 +138,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
       __syncthreads();
       const float amax = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
       par ^= 1;
-      scale = amax == 0.0f ? 1.0f : amax / (float)kQmax;
-      rsc = 1.0 / (double)scale;
+      scale = amax == 0.0f ? 1.0f : amax / (F8 ? kF8max : (float)kQmax);
+      rsc = amax == 0.0f ? 0.0 : 1.0 / (double)scale;   // a zero row: every code 0
     }
     if (tid == 0) scale_out[r] = scale;
 #pragma unroll
@@ -142,10 +147,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
       const int64_t c = (int64_t)j * 256 + tid;
       if (FULL || c < nchunks) {
         uint2 o;
-        o.x = pack4_lowbytes(quant_code_bits(v[j][0], rsc), quant_code_bits(v[j][1], rsc),
-                             quant_code_bits(v[j][2], rsc), quant_code_bits(v[j][3], rsc));
-        o.y = pack4_lowbytes(quant_code_bits(v[j][4], rsc), quant_code_bits(v[j][5], rsc),
-                             quant_code_bits(v[j][6], rsc), quant_code_bits(v[j][7], rsc));
+        if (F8) {
+          // exact quotients, then the E4M3 conversion; a zero row (rsc = 0) is
+          // written as zero codes
+          float q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = div_by_recip(v[j][e], rsc);
+          o.x = rsc == 0.0 ? 0u : e4m3_pack4(q[0], q[1], q[2], q[3]);
+          o.y = rsc == 0.0 ? 0u : e4m3_pack4(q[4], q[5], q[6], q[7]);
+        } else {
+          o.x = pack4_lowbytes(quant_code_bits(v[j][0], rsc), quant_code_bits(v[j][1], rsc),
+                               quant_code_bits(v[j][2], rsc), quant_code_bits(v[j][3], rsc));
+          o.y = pack4_lowbytes(quant_code_bits(v[j][4], rsc), quant_code_bits(v[j][5], rsc),
+                               quant_code_bits(v[j][6], rsc), quant_code_bits(v[j][7], rsc));
+        }
         *reinterpret_cast<uint2*>(Q + r * K + c * 8) = o;
       }
     }
@@ -180,7 +195,7 @@ template <typename T> __device__ __forceinline__ float load1(const T* p);
 template <> __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool F8>
 __global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restrict__ A, int64_t R,
                                                               int64_t K, const float* __restrict__ s,
                                                               const float* __restrict__ clip,
@@ -209,12 +224,16 @@ __global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restric
       const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
       __syncthreads();
       zero = amax == 0.0f;
-      scale = zero ? 1.0f : amax / (float)kQmax;
+      scale = zero ? 1.0f : amax / (F8 ? kF8max : (float)kQmax);
     }
     if (tid == 0) scale_out[r] = scale;
     for (int64_t k = tid; k < K; k += 256) {
       float x = load1<T>(row + k);
       if (s) x = (MODE == 1) ? x * s[k] : x / s[k];
+      if (F8) {
+        Q[r * K + k] = (int8_t)(zero ? 0u : e4m3_code(x / scale));
+        continue;
+      }
       float q = zero ? 0.0f : __builtin_rintf(x / scale);
       q = fminf(fmaxf(q, -(float)kQmax), (float)kQmax);
       Q[r * K + k] = (int8_t)(int)q;
@@ -222,7 +241,7 @@ __global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restric
   }
 }
 
-template <typename T, int MODE, bool HAS_S>
+template <typename T, int MODE, bool HAS_S, bool F8>
 static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, const float* clip,
                              int8_t* Q, float* scale, int ncu, hipStream_t st) {
   const int64_t nchunks = K / 8;
@@ -232,8 +251,8 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, c
   const int c2 = cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8;   // instantiated sizes
   const bool full = K == (int64_t)c2 * 2048;
 #define SQ_QUANT_LAUNCH(C)                                                                              \
-  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true>), grid, block, 0, st, A, R, K, s, clip, Q, scale); \
-  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false>), grid, block, 0, st, A, R, K, s, clip, Q, scale);
+  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true, F8>), grid, block, 0, st, A, R, K, s, clip, Q, scale); \
+  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false, F8>), grid, block, 0, st, A, R, K, s, clip, Q, scale);
   switch (c2) {
     case 1: SQ_QUANT_LAUNCH(1) break;
     case 2: SQ_QUANT_LAUNCH(2) break;
@@ -244,15 +263,15 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, c
   return hipGetLastError();
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool F8 = false>
 static hipError_t quant_dispatch(const T* A, int64_t R, int64_t K, const float* s, const float* clip,
                                  int8_t* Q, float* scale, bool vec_ok, int ncu, hipStream_t st) {
   if (vec_ok && K <= kQuantFastMaxK) {
-    return s ? quant_fast<T, MODE, true>(A, R, K, s, clip, Q, scale, ncu, st)
-             : quant_fast<T, MODE, false>(A, R, K, s, clip, Q, scale, ncu, st);
+    return s ? quant_fast<T, MODE, true, F8>(A, R, K, s, clip, Q, scale, ncu, st)
+             : quant_fast<T, MODE, false, F8>(A, R, K, s, clip, Q, scale, ncu, st);
   }
   int64_t g = R < 8LL * ncu ? R : 8LL * ncu;
-  hipLaunchKernelGGL((quant_rows_slow_kernel<T, MODE>), dim3((unsigned)g), dim3(256), 0, st, A, R, K,
+  hipLaunchKernelGGL((quant_rows_slow_kernel<T, MODE, F8>), dim3((unsigned)g), dim3(256), 0, st, A, R, K,
                      s, clip, Q, scale);
   return hipGetLastError();
 }
@@ -264,6 +283,8 @@ static hipError_t quant_mode(const T* A, int mode, int64_t R, int64_t K, const f
   switch (mode) {
     case kQuantWeights: return quant_dispatch<T, 1>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
     case kQuantActStatic: return quant_dispatch<T, 2>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    case kQuantActF8: return quant_dispatch<T, 0, true>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    case kQuantWeightsF8: return quant_dispatch<T, 1, true>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
     default: return quant_dispatch<T, 0>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
   }
 }

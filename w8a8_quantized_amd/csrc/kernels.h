@@ -21,8 +21,9 @@ hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, flo
 // Row quantiser modes: per-token activations (divide by s, per-row range),
 // per-output-channel weights (multiply by s, per-row range; also the
 // decomposition's bulk rows, with s a 0/1 column mask), activations against the
-// range *clip (divide by s, one scale for every row).
-enum QuantMode { kQuantAct = 0, kQuantWeights = 1, kQuantActStatic = 2 };
+// range *clip (divide by s, one scale for every row); and the first two with FP8
+// E4M3 codes (scale = row amax / 448).
+enum QuantMode { kQuantAct = 0, kQuantWeights = 1, kQuantActStatic = 2, kQuantActF8 = 3, kQuantWeightsF8 = 4 };
 hipError_t launch_quant_rows(const void* A, bool bf16, int mode, int64_t R, int64_t K,
                              const float* s, const float* clip, int8_t* Q, float* scale,
                              bool vec_ok, int ncu, hipStream_t st);
@@ -60,6 +61,8 @@ struct GemmArgs {
   const float* xo = nullptr;
   const float* wo = nullptr;
   int64_t n_o = 0;
+  // FP8 E4M3 operand bytes (binary32 accumulation; float outputs only)
+  bool f8 = false;
 };
 
 // Prefill-shaped GEMM on the int8 MFMA units (K % 16 == 0, 16-byte aligned operands).

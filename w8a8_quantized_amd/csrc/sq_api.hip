@@ -48,16 +48,17 @@ sq_status check_gemm_args(const int8_t* Xq, const float* xs, const int8_t* Wq, c
 
 sq_status run_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws, int64_t T,
                    int64_t N, int64_t K, void* Y, sq_dtype y_t, hipStream_t st,
-                   const float* xo = nullptr, const float* wo = nullptr, int64_t n_o = 0) {
+                   const float* xo = nullptr, const float* wo = nullptr, int64_t n_o = 0,
+                   bool f8 = false) {
   sq::GemmArgs a;
   a.Xq = Xq; a.xs = xs; a.Wq = Wq; a.ws = ws;
   a.T = T; a.N = N; a.K = K; a.Y = Y;
-  a.xo = xo; a.wo = wo; a.n_o = n_o;
+  a.xo = xo; a.wo = wo; a.n_o = n_o; a.f8 = f8;
   a.out = y_t == SQ_F32 ? sq::kOutF32 : (y_t == SQ_BF16 ? sq::kOutBF16 : sq::kOutI32);
   a.vec_store = (N % 4 == 0) && aligned16(Y) && (y_t == SQ_I32 || aligned16(ws));
   const bool mfma_ok = (K % 16 == 0) && aligned16(Xq) && aligned16(Wq);
   if (!mfma_ok) return hip_status(sq::launch_gemm_generic(a, st));
-  if (T <= sq::kDecodeMaxT) return hip_status(sq::launch_gemv_mfma(a, cu_count(), st));
+  if (T <= sq::kDecodeMaxT && !f8) return hip_status(sq::launch_gemv_mfma(a, cu_count(), st));
   return hip_status(sq::launch_gemm_mfma(a, cu_count(), st));
 }
 
@@ -251,6 +252,36 @@ sq_status sq_decomp_gemm(const int8_t* Xq, const float* x_scale, const int8_t* W
   if (n_o > 0 && (!X_out || !W_out)) return SQ_ERR_NULL;
   if (n_o > 0 && (!aligned16(X_out) || !aligned16(W_out))) return SQ_ERR_ARG;
   return run_gemm(Xq, x_scale, Wq, w_scale, T, N, K, Y, y_t, stream, X_out, W_out, n_o);
+}
+
+sq_status sq_quantize_weights_fp8(const void* W, sq_dtype w_t, int64_t N, int64_t K, const float* s,
+                                  uint8_t* Wq, float* w_scale, hipStream_t stream) {
+  if (!W || !Wq || !w_scale) return SQ_ERR_NULL;
+  if (!in_dtype(w_t)) return SQ_ERR_DTYPE;
+  if (N < 1 || K < 1) return SQ_ERR_SHAPE;
+  const bool vec = (K % 8 == 0) && rows_vec16(W, K, esize(w_t)) && aligned16(Wq);
+  return hip_status(sq::launch_quant_rows(W, w_t == SQ_BF16, sq::kQuantWeightsF8, N, K, s, nullptr,
+                                          reinterpret_cast<int8_t*>(Wq), w_scale, vec, cu_count(), stream));
+}
+
+sq_status sq_quant_act_fp8(const void* X, sq_dtype x_t, int64_t T, int64_t K, const float* s, uint8_t* Xq,
+                           float* x_scale, hipStream_t stream) {
+  sq_status r = check_act_args(X, x_t, T, K);
+  if (r != SQ_OK) return r;
+  if (!Xq || !x_scale) return SQ_ERR_NULL;
+  const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
+  return hip_status(sq::launch_quant_rows(X, x_t == SQ_BF16, sq::kQuantActF8, T, K, s, nullptr,
+                                          reinterpret_cast<int8_t*>(Xq), x_scale, vec, cu_count(), stream));
+}
+
+sq_status sq_fp8_gemm(const uint8_t* Xq, const float* x_scale, const uint8_t* Wq, const float* w_scale,
+                      int64_t T, int64_t N, int64_t K, void* Y, sq_dtype y_t, hipStream_t stream) {
+  const int8_t* xq = reinterpret_cast<const int8_t*>(Xq);
+  const int8_t* wq = reinterpret_cast<const int8_t*>(Wq);
+  sq_status r = check_gemm_args(xq, x_scale, wq, w_scale, T, N, K, Y, y_t);
+  if (r != SQ_OK) return r;
+  if (y_t == SQ_I32) return SQ_ERR_DTYPE;
+  return run_gemm(xq, x_scale, wq, w_scale, T, N, K, Y, y_t, stream, nullptr, nullptr, 0, true);
 }
 
 sq_status sq_w8a8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,

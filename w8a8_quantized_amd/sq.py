@@ -45,6 +45,9 @@ _SIGS = {
     "sq_decomp_prepare_weights": ([_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P], _I),
     "sq_decomp_quant_act": ([_P, _I, _I64, _I64, _P, _P, _I64, _P, _P, _P, _P], _I),
     "sq_decomp_gemm": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _P], _I),
+    "sq_quantize_weights_fp8": ([_P, _I, _I64, _I64, _P, _P, _P, _P], _I),
+    "sq_quant_act_fp8": ([_P, _I, _I64, _I64, _P, _P, _P, _P], _I),
+    "sq_fp8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_linear_workspace_size": ([_I64, _I64], _SZ),
     "sq_w8a8_linear": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
@@ -271,6 +274,45 @@ def sq_decomp_gemm(Xq, x_scale, Wq, w_scale, X_out, W_out, out_dtype=torch.bfloa
     _check(_lib.sq_decomp_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale),
                                _ptr(X_out) if n_o else None, _ptr(W_out) if n_o else None, T, N, K, n_o,
                                _ptr(Y), yt, _stream(Xq.device)))
+    return Y
+
+
+def sq_quantize_weights_fp8(W, s=None, Wq=None, w_scale=None):
+    """Per-output-channel FP8 E4M3 codes (uint8) of W diag(s).  Returns (Wq, w_scale)."""
+    N, K = W.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    Wq = _want(Wq, (N, K), torch.uint8, W.device)
+    w_scale = _want(w_scale, (N,), torch.float32, W.device)
+    _check(_lib.sq_quantize_weights_fp8(_ptr(W), _dt(W), N, K, _ptr(s), _ptr(Wq), _ptr(w_scale),
+                                        _stream(W.device)))
+    return Wq, w_scale
+
+
+def sq_quant_act_fp8(X, s=None, Xq=None, x_scale=None):
+    """Per-token FP8 E4M3 codes (uint8) of X diag(s)^-1.  Returns (Xq, x_scale)."""
+    T, K = X.shape
+    if s is not None and s.numel() != K:
+        raise ValueError("s must have K entries")
+    Xq = _want(Xq, (T, K), torch.uint8, X.device)
+    x_scale = _want(x_scale, (T,), torch.float32, X.device)
+    _check(_lib.sq_quant_act_fp8(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(Xq), _ptr(x_scale),
+                                 _stream(X.device)))
+    return Xq, x_scale
+
+
+def sq_fp8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
+    """Y = dequant(e4m3(Xq) @ e4m3(Wq)^T) on the FP8 matrix cores."""
+    T, K = Xq.shape
+    N, K2 = Wq.shape
+    if K != K2 or Xq.dtype != torch.uint8 or Wq.dtype != torch.uint8:
+        raise ValueError("Xq [T, K] and Wq [N, K] must be uint8 E4M3 codes with the same K")
+    yt = _DT.get(out_dtype)
+    if yt is None or out_dtype == torch.int32:
+        raise ValueError(f"out_dtype {out_dtype} not accepted")
+    Y = _want(Y, (T, N), out_dtype, Xq.device)
+    _check(_lib.sq_fp8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), T, N, K, _ptr(Y), yt,
+                            _stream(Xq.device)))
     return Y
 
 
