@@ -134,6 +134,34 @@ __global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A
   }
 }
 
+// Column-block form (used for fp32): the 256 threads of a workgroup sit side by
+// side over a block of 256 16-byte column chunks (4 KB of each row) and walk the
+// rows of a tall slab with U rows of loads in flight, then issue one atomic max
+// per column.  One workgroup per CU (8192 x 8192 fp32: 46.6 us against 54.9 us
+// for the slab form, whose 4 waves split the rows of short slabs; for bf16 the
+// slab form stays ahead).  The last group reuses row r1 - 1 for rows past the
+// slab end (harmless for a maximum), so the loads carry no conditions.
+template <typename T, int VEC, int U>
+__global__ __launch_bounds__(256) void col_absmax_blk_kernel(const T* __restrict__ A, int64_t rows,
+                                                             int64_t cols, int64_t slab,
+                                                             float* __restrict__ amax) {
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VEC;
+  if (c0 >= cols) return;   // cols % VEC == 0 on this path
+  const int64_t r0 = (int64_t)blockIdx.y * slab;
+  const int64_t r1 = r0 + slab < rows ? r0 + slab : rows;
+  ColMax<T, VEC> acc;
+  acc.init();
+  const T* p = A + c0;
+  for (int64_t r = r0; r < r1; r += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc.add(p + (r + u < r1 ? r + u : r1 - 1) * cols);
+  }
+  float m[VEC];
+  acc.result(m);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) atomicMax(reinterpret_cast<unsigned int*>(amax + c0 + i), __float_as_uint(m[i]));
+}
+
 // Range of the whole smoothed activation tensor, max over t, k of
 // |fl32(A_tk / s_k)| (the per-tensor activation levels of multigrid.ai
 // "SmoothQuant Explained", section "Where it fits, and where it does not").
@@ -302,8 +330,20 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
                   : col_absmax_t<uint16_t, 1, 4>(a, rows, cols, amax, ncu, st);
   }
   const float* a = static_cast<const float*>(A);
-  return vec_ok ? col_absmax_t<float, 4, 16>(a, rows, cols, amax, ncu, st)
-                : col_absmax_t<float, 1, 4>(a, rows, cols, amax, ncu, st);
+  if (vec_ok) {
+    const int64_t cb = (cols / 4 + 255) / 256;          // column blocks
+    int64_t slabs = ncu / cb;
+    if (slabs < 1) slabs = 1;
+    const int64_t max_slabs = (rows + 15) / 16;          // at least 16 rows per slab
+    if (slabs > max_slabs) slabs = max_slabs;
+    if (slabs > 65535) slabs = 65535;
+    const int64_t slab = (rows + slabs - 1) / slabs;
+    slabs = (rows + slab - 1) / slab;
+    hipLaunchKernelGGL((col_absmax_blk_kernel<float, 4, 16>), dim3((unsigned)cb, (unsigned)slabs), dim3(256), 0,
+                       st, a, rows, cols, slab, amax);
+    return hipGetLastError();
+  }
+  return col_absmax_t<float, 1, 4>(a, rows, cols, amax, ncu, st);
 }
 
 template <typename T, int VEC, int U>
