@@ -1,6 +1,7 @@
 """Throughput of the SmoothQuant W8A8 linear layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-decode]
+    python bench.py --configs      # per-configuration figures, one JSON object per line
 
 One step is one pass of the whole path over one batch of synthetic input, all
 through libsq.so on the current HIP stream:
@@ -210,6 +211,49 @@ def decomp_measure(sq, torch):
     return out
 
 
+def configs_report(sq, torch):
+    """Per-configuration figures (one JSON object per line, not the contract
+    line): the run-time layer (sq_quant_act + sq_w8a8_gemm) on each named
+    workload with its own smoothing factors, timed as back-to-back calls.  The
+    large inputs are rotated over three copies when they exceed the Infinity
+    Cache."""
+    import workloads as WL
+    dev = torch.device("cuda")
+    for name in WL.WORKLOADS:
+        w = WL.make(name)
+        T, N, K = w.T, w.N, w.K
+        xdt = torch.bfloat16 if w.x_dtype == "bf16" else torch.float32
+        ydt = torch.bfloat16 if w.y_dtype == "bf16" else torch.float32
+        X = torch.from_numpy(w.X).to(xdt).to(dev)
+        Xs = X if w.X_calib is None else torch.from_numpy(w.X_calib).to(xdt).to(dev)
+        W = torch.from_numpy(w.W).to(dev)
+        s, _, _ = sq.sq_smooth_scales(Xs, W, w.alpha)
+        Wq, ws = sq.sq_quantize_weights(W, s)
+        del W
+        torch.cuda.empty_cache()
+        Xq, xs = sq.sq_quant_act(X, s)
+        Y = torch.empty((T, N), dtype=ydt, device=dev)
+        big = N * K > 128 << 20
+        Wc = [Wq] + ([Wq.clone() for _ in range(2)] if big else [])
+        Xc = [X] + ([X.clone() for _ in range(2)] if T * K * X.element_size() > 128 << 20 else [])
+        t_q = _time_calls(torch, lambda x_: sq.sq_quant_act(x_, s, Xq=Xq, x_scale=xs), Xc)
+        t_g = _time_calls(torch, lambda wq: sq.sq_w8a8_gemm(Xq, xs, wq, ws, out_dtype=ydt, Y=Y), Wc)
+        ops = 2.0 * T * N * K
+        gb = _gemm_bytes(T, N, K, 2 if ydt == torch.bfloat16 else 4)
+        qb = _quant_bytes(T, K, X.element_size())
+        print(json.dumps({"workload": name, "T": T, "N": N, "K": K, "alpha": w.alpha,
+                          "linear_TOPS": ops / ((t_q + t_g) * 1e-3) / 1e12,
+                          "gemm_us": t_g * 1e3, "gemm_TOPS": ops / (t_g * 1e-3) / 1e12,
+                          "gemm_frac_int8_peak": ops / (t_g * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                          "gemm_GB/s": gb / (t_g * 1e-3) / 1e9,
+                          "gemm_frac_hbm": gb / (t_g * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "quant_us": t_q * 1e3, "quant_GB/s": qb / (t_q * 1e-3) / 1e9,
+                          "quant_frac_hbm": qb / (t_q * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "copies_rotated": len(Wc)}), flush=True)
+        del X, Xs, Wq, Xq, Y, Wc, Xc
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +262,8 @@ def main():
     ap.add_argument("--workload", default="heavy_t8192_k8192_n8192")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="print per-configuration figures for every named workload instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -233,6 +279,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.configs:
+        configs_report(sq, torch)
+        return
     w = WL.make(args.workload)
     T, N, K = w.T, w.N, w.K
     xdt = torch.bfloat16 if w.x_dtype == "bf16" else torch.float32

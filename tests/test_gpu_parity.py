@@ -141,8 +141,10 @@ def _codes(rng, r, k):
 GEMM_SHAPES = [
     # decode kernel (T <= 64)
     (1, 1, 16), (1, 40, 64), (5, 129, 80), (16, 1000, 256), (17, 77, 1040), (33, 64, 48), (64, 300, 528),
-    # prefill kernel, 128x128 tiles, ragged edges and K tails
+    # prefill kernel, 64x64 tiles (< 256 tiles of 128x128), ragged edges and K tails
     (65, 40, 16), (100, 129, 64), (300, 1000, 80), (257, 513, 1040), (512, 1024, 4096),
+    # prefill kernel, 128x128 tiles (>= 256 of them, < 256 of 256x256), ragged edges and K tails
+    (1000, 4100, 272), (1100, 4000, 1040),
     # prefill kernel, 256x256 tiles (>= 256 tiles), ragged edges and a K tail
     (2100, 8200, 48), (2048, 8192, 64),
     # generic kernel (K % 16 != 0)
@@ -161,7 +163,7 @@ def test_gemm_int32_accumulators(sq, T, N, K):
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("T,N,K", [(1, 40, 64), (17, 77, 1040), (300, 1000, 80), (2100, 8200, 48),
-                                   (70, 33, 83), (64, 130, 64), (129, 257, 64)])
+                                   (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272)])
 def test_gemm_epilogue(sq, out, T, N, K):
     rng = np.random.default_rng(T + N + K)
     Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)

@@ -277,16 +277,26 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
   };
   // wait until at most `later` stages of this wave's DMA loads are in flight
   // (and, for wait_vm_lds, its LDS reads are complete)
+  // (the counter limit is 63 loads; deeper rings wait conservatively)
   auto wait_vm = [&](int later) {
-    if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_enc(3 * PER));
-    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * PER));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(PER));
+    static_assert(PER <= 63, "loads per stage");
+    if (later >= 7 && 7 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(7 * PER <= 63 ? 7 * PER : 0));
+    else if (later >= 6 && 6 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(6 * PER <= 63 ? 6 * PER : 0));
+    else if (later >= 5 && 5 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(5 * PER <= 63 ? 5 * PER : 0));
+    else if (later >= 4 && 4 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(4 * PER <= 63 ? 4 * PER : 0));
+    else if (later >= 3 && 3 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(3 * PER <= 63 ? 3 * PER : 0));
+    else if (later >= 2 && 2 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * PER <= 63 ? 2 * PER : 0));
+    else if (later >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(PER));
     else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
   };
   auto wait_vm_lds = [&](int later) {
-    if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_enc(3 * PER) & kLgkm0);
-    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * PER) & kLgkm0);
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(PER) & kLgkm0);
+    if (later >= 7 && 7 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(7 * PER <= 63 ? 7 * PER : 0) & kLgkm0);
+    else if (later >= 6 && 6 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(6 * PER <= 63 ? 6 * PER : 0) & kLgkm0);
+    else if (later >= 5 && 5 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(5 * PER <= 63 ? 5 * PER : 0) & kLgkm0);
+    else if (later >= 4 && 4 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(4 * PER <= 63 ? 4 * PER : 0) & kLgkm0);
+    else if (later >= 3 && 3 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(3 * PER <= 63 ? 3 * PER : 0) & kLgkm0);
+    else if (later >= 2 && 2 * PER <= 63) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * PER <= 63 ? 2 * PER : 0) & kLgkm0);
+    else if (later >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(PER) & kLgkm0);
     else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0) & kLgkm0);
   };
   auto bar = [&] {
@@ -542,12 +552,17 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
     if (big8 >= ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true>(a, st);
     return gemm_cfg<128, 128, 128, 2, 2, 2, true>(a, st);
   }
-  // 256x256 tiles when they fill the chip at least once, else 128x128.  The big
-  // tile runs 16 waves of 64x64 (4 per SIMD): with fewer, larger wave tiles the
-  // per-stage barrier and LDS latency are not covered (measured ~8% slower).
+  // 256x256 tiles when they fill the chip at least once; the big tile runs 16
+  // waves of 64x64 (4 per SIMD): with fewer, larger wave tiles the per-stage
+  // barrier and LDS latency are not covered (measured ~8% slower).  Smaller
+  // problems are latency-bound: 128x128 tiles, else 64x64 tiles, both with a
+  // 4-deep ring (two workgroups per CU for 64x64): 512x4096x4096 18.2 us and
+  // 128x1024x1024 5.5 us, against 25.8 and 8.4 us with 128x128 and 2 stages.
   const int64_t big = ((a.N + 255) / 256) * ((a.T + 255) / 256);
   if (big >= ncu) return gemm_cfg<256, 256, 128, 4, 4, 2>(a, st);
-  return gemm_cfg<128, 128, 128, 2, 2, 2>(a, st);
+  const int64_t mid = ((a.N + 127) / 128) * ((a.T + 127) / 128);
+  if (mid >= ncu) return gemm_cfg<128, 128, 128, 2, 2, 4>(a, st);
+  return gemm_cfg<64, 64, 128, 2, 2, 4>(a, st);
 }
 
 // ---------------------------------------------------------------- generic path
