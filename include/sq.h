@@ -326,7 +326,8 @@ sq_status sq_quant_act_fp8(const void *X, sq_dtype x_t, int64_t T, int64_t K, co
  * values is exact, but the hardware sums them at less than full binary32
  * precision when their magnitudes differ widely, so acc is not the exact sum:
  * it is within 2^-10 * sum_k |products| of it (a measured property of the
- * instruction; the exact sum is the reference).  y_t = SQ_F32 or SQ_BF16.
+ * instruction; the exact sum is the reference).  y_t = SQ_F32 or SQ_BF16;
+ * K <= SQ_MAX_K as for sq_w8a8_gemm.
  */
 sq_status sq_fp8_gemm(const uint8_t *Xq, const float *x_scale, const uint8_t *Wq,
                       const float *w_scale, int64_t T, int64_t N, int64_t K, void *Y,

@@ -11,14 +11,20 @@
 // Prefill kernel: v_mfma_i32_32x32x32_i8.  Both operands are K-contiguous, so the
 // MFMA "A" operand is a 32-row block of Wq (rows = output channels) and the "B"
 // operand a 32-row block of Xq (rows = tokens); a lane then ends up holding four
-// consecutive output channels of one token, which the epilogue writes as one
-// 8-byte (bf16) or 16-byte (fp32/int32) store.  Tiles of Wq and Xq are staged
-// through LDS in a double buffer (one barrier per K stage); the 16-byte chunk
-// position within each LDS row is XOR-swizzled by the row index so that both the
-// staging writes and the fragment reads (32 rows, same column) are free of bank
-// conflicts.  Workgroups are remapped so that each XCD (which owns a private L2)
-// works through a contiguous run of tiles, grouped 8 output-channel tiles wide,
-// which keeps the operand panels it streams shared inside that L2.
+// consecutive output channels of one token, which the epilogue stages through
+// LDS and writes as whole row segments.  Tiles of Wq and Xq are staged through an
+// LDS ring of 2 (large problems) or 4 (small, latency-bound problems) K stages,
+// one barrier per stage; the 16-byte chunk position within each LDS row is
+// XOR-swizzled by the row index so that both the staging writes and the fragment
+// reads (32 rows, same column) are free of bank conflicts.  Workgroups are
+// remapped so that each XCD (which owns a private L2) works through a contiguous
+// run of tiles, grouped 8 output-channel tiles wide, which keeps the operand
+// panels it streams shared inside that L2.
+//
+// The same kernel serves two variants: the mixed-precision decomposition (a
+// binary32 outlier-channel product added in the epilogue) and FP8 E4M3 operands
+// on the FP8 matrix cores (binary32 accumulators); both are described at the
+// kernel.
 #include <type_traits>
 
 #include "common.h"

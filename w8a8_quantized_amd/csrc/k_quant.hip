@@ -14,8 +14,8 @@
 // and walks rows r = blockIdx.x, blockIdx.x + gridDim.x, ...  Per-column factors
 // (the binary64 reciprocal of s for the division, or s itself for the multiply)
 // therefore stay in registers across all of the workgroup's rows.  Each row is
-// read from HBM once, held in registers, reduced to its absmax (wave shuffle +
-// a 4-entry LDS exchange, one barrier), then turned into codes and written with
+// read from HBM once, held in registers, reduced to its absmax (DPP wave
+// reduction + a 4-entry LDS exchange, one barrier), then turned into codes and written with
 // 8-byte stores.  The next row's loads are issued before the current row is
 // processed.  Both divisions of the method are done exactly as a multiply by a
 // binary64 reciprocal (see div_by_recip).
@@ -29,7 +29,11 @@
 //
 // FP8 mode (F8): the same round trip on the E4M3 grid (inferenceinterviews.com,
 // formats paragraph: per-token FP8 activations): scale = amax / 448, code = the
-// E4M3 value nearest to v / scale (ties to even), saturated at +-448.
+// E4M3 value nearest to v / scale (ties to even), saturated at +-448; the exact
+// binary32 quotient goes through the hardware conversion (see e4m3_pack4).
+//
+// The multiply mode (MODE 1) also serves the mixed-precision decomposition's
+// bulk rows, weights and activations alike, with s a 0/1 column mask.
 //
 // Slow path (any shape/alignment): one workgroup per row, two passes over the
 // row with plain IEEE binary32 divisions; identical results.

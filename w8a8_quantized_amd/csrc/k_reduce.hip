@@ -3,12 +3,14 @@
 // Column absmax (inferenceinterviews.com "Why do activation outliers break INT8
 // W8A8...", section "A strong answer": max over tokens t of |X_tj| and over
 // output rows n of |W_nj|) is a pure HBM stream: each element is read once.
-// A workgroup is 4 waves; its 64 lanes each own one 16-byte column chunk and the
-// 4 waves walk interleaved rows of a row slab, so every wave load is 1 KB of one
-// row (fully coalesced), with 8-16 rows per wave in flight.  The 4 partial
-// maxima meet in LDS and one atomic max per column and slab goes to the output.  |x| >= 0, so the unsigned order of
-// the binary32 bit patterns is the numeric order and an integer atomic max is
-// exact.
+// Two forms: a slab form (bf16) in which a workgroup's 64 lanes each own one
+// 16-byte column chunk and its 4 waves walk interleaved rows of a short row
+// slab, so every wave load is 1 KB of one row, the 4 partial maxima meeting in
+// LDS; and a column-block form (fp32) described at its kernel.  Either way one
+// atomic max per column and slab goes to the output: |x| >= 0, so the unsigned
+// order of the binary32 bit patterns is the numeric order and an integer atomic
+// max is exact.  The per-tensor range of the smoothed activations and the
+// smoothing factors are here too.
 #include "common.h"
 #include "kernels.h"
 
