@@ -83,7 +83,7 @@ def _omp_threads():
         return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
-def cpu_baseline(w, target_s=12.0):
+def cpu_baseline(w, target_s=15.0):
     """The oracle as it stands, on a prefix of the workload's tokens: statistics,
     smoothing factors and weight quantisation in full, then quantisation, integer
     GEMM, epilogue and bf16 rounding for `tokens` tokens.  Throughput in TOPS of
@@ -105,7 +105,7 @@ def cpu_baseline(w, target_s=12.0):
             O.to_bf16(y)
 
     s, Wq, ws = offline()
-    probe = min(8, w.T)
+    probe = min(64, w.T)   # enough rows for the OpenMP loops to spread over the cores
     t0 = time.perf_counter()
     runtime(s, Wq, ws, probe)
     per_token = (time.perf_counter() - t0) / probe
