@@ -323,7 +323,8 @@ def main():
     if torch.distributed.is_available() and torch.distributed.is_initialized():
         torch.distributed.barrier()
     ms_step = wall * 1e3 / args.steps
-    t_gemm = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    launch_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_gemm = float(np.mean(launch_ms))
 
     # per-call breakdown outside the timed region: each entry point launched
     # `reps` times back to back between two events (launch gaps amortised),
@@ -389,7 +390,8 @@ def main():
                      "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": _gemm_traffic(w.name),
                      "traffic_unit": "bytes per launch (memory side, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                     "per_launch_ops": ops, "avg_launch_ms": t_gemm},
+                     "per_launch_ops": ops, "avg_launch_ms": t_gemm,
+                     "launch_ms_p10_p50_p90": [float(np.percentile(launch_ms, q)) for q in (10, 50, 90)]},
         "breakdown_ms_batched": {"smooth_scales": t_smooth, "quantize_weights": t_wq,
                                  "quant_act": t_quant, "w8a8_gemm": t_gemm_b},
         "linear_tops": ops / ((t_quant + t_gemm) * 1e-3) / 1e12,
