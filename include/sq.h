@@ -222,8 +222,10 @@ sq_status sq_fold_norm_gain(const float *v, const float *s, int64_t K, float *ou
  *   LayerNorm  mean_t = mean_k X[t][k],
  *              rstd_t = 1 / sqrt(mean_k (X[t][k] - mean_t)^2 + eps)
  *              h[t][k] = ((X[t][k] - mean_t) * rstd_t) * gain[k] + bias[k]
- * The statistics are summed in binary64 and rounded once to binary32; h is
- * binary32, one rounding per operation in the order written.  Then h is
+ * The statistics are rounded once to binary32 and are within 1e-6 relative of
+ * their binary64 values (sums in binary64 except within 8-element chunks of
+ * squares); h is binary32, one rounding per operation in the order written,
+ * from those binary32 statistics.  Then h is
  * quantised exactly as sq_quant_act quantises X_hat (x_scale[t] = max_k |h| / 127,
  * scale 1 and codes 0 for a zero row).  X is read once; h is never stored.
  *   X          device, x_t = SQ_F32 or SQ_BF16, [T][K] (the norm's input)
