@@ -81,6 +81,26 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 #pragma unroll
   for (int b = 0; b < TB; ++b) xoff[b] = (b * 16 + fi) * K + fg * 16;
 
+  // The epilogue's scale factors are fetched before the K loop: loaded after it,
+  // they would add one more memory round trip to the end of every workgroup.
+  float xsv[TB], wsv[NB][4];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) xsv[b] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wsv[i][e] = 0.0f;
+  if (OUT != kOutI32 && kw == 0) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if (b * 16 + fi < T) xsv[b] = xs[b * 16 + fi];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n0 + i * 16 + 4 * fg + e < N) wsv[i][e] = ws[n0 + i * 16 + 4 * fg + e];
+  }
+
   v4i acc[NB][TB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
@@ -169,10 +189,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
         else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = a4[e];
         continue;
       }
-      const float sc = xs[t];
+      const float sc = xsv[b];
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (sc * ws[n + e]) : 0.0f;
+      for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (sc * wsv[i][e]) : 0.0f;
       if (OUTL) {
         // binary32 outlier-channel product, o ascending; loads 8 outliers ahead
         float so[4] = {0.f, 0.f, 0.f, 0.f};
