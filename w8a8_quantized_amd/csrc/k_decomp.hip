@@ -22,34 +22,75 @@ namespace sq {
 
 // mask[j] = 0 when column j is among the n_o columns with the largest absmax
 // (ties to the lower index), else 1.  rank_j = #{i : a_i > a_j or (a_i == a_j and
-// i < j)}; each workgroup stages tiles of the vector in LDS.
+// i < j)}, a permutation of 0..K-1.  A workgroup owns 64 columns j (one per lane);
+// its four waves split each 1024-value LDS tile of the vector in quarters and read
+// it four values at a time; the four partial counts meet in LDS.  Tile entries
+// past K hold -inf at indices >= K > j, so they never count.
 __global__ __launch_bounds__(256) void decomp_rank_kernel(const float* __restrict__ a, int64_t K,
                                                           int64_t n_o, float* __restrict__ mask) {
-  __shared__ float tile[256];
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float4 tile[256];
+  __shared__ int part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + lane;
   const float aj = j < K ? a[j] : 0.0f;
-  int64_t rank = 0;
-  for (int64_t i0 = 0; i0 < K; i0 += 256) {
+  int rank = 0;
+  for (int64_t i0 = 0; i0 < K; i0 += 1024) {
     __syncthreads();
-    tile[threadIdx.x] = i0 + threadIdx.x < K ? a[i0 + threadIdx.x] : 0.0f;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = i0 + 4 * threadIdx.x + e;
+      v[e] = i < K ? a[i] : -__builtin_inff();
+    }
+    tile[threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
     __syncthreads();
-    const int lim = K - i0 < 256 ? (int)(K - i0) : 256;
-    for (int u = 0; u < lim; ++u) {
-      const float ai = tile[u];
-      rank += (ai > aj) || (ai == aj && i0 + u < j);
+    const int64_t left = K - i0 - 256 * wave;   // values of this wave's quarter that exist
+    const int nq = left <= 0 ? 0 : (left >= 256 ? 64 : (int)((left + 3) / 4));
+    for (int q = 0; q < nq; ++q) {
+      const float4 t = tile[wave * 64 + q];
+      const int64_t ib = i0 + 256 * wave + 4 * q;
+      rank += (t.x > aj) || (t.x == aj && ib < j);
+      rank += (t.y > aj) || (t.y == aj && ib + 1 < j);
+      rank += (t.z > aj) || (t.z == aj && ib + 2 < j);
+      rank += (t.w > aj) || (t.w == aj && ib + 3 < j);
     }
   }
-  if (j < K) mask[j] = rank < n_o ? 0.0f : 1.0f;
+  part[wave][lane] = rank;
+  __syncthreads();
+  if (wave == 0 && j < K) {
+    const int r = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    mask[j] = r < n_o ? 0.0f : 1.0f;
+  }
 }
 
-// idx[p] = the p-th column (ascending) whose mask is 0.
-__global__ __launch_bounds__(256) void decomp_index_kernel(const float* __restrict__ mask, int64_t K,
-                                                           int32_t* __restrict__ idx) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= K || mask[j] != 0.0f) return;
-  int64_t p = 0;
-  for (int64_t i = 0; i < j; ++i) p += mask[i] == 0.0f;
-  idx[p] = (int32_t)j;
+// idx[p] = the p-th column (ascending) whose mask is 0.  One workgroup: each
+// thread counts the zeros of its contiguous share of the mask, an exclusive scan
+// of the counts in LDS gives each share's first position, and each thread writes
+// the indices of its share's zeros.  Positions past n_o are not written (the
+// mask has exactly n_o zeros unless the absmax vector holds a NaN).
+__global__ __launch_bounds__(1024) void decomp_index_kernel(const float* __restrict__ mask, int64_t K,
+                                                            int64_t n_o, int32_t* __restrict__ idx) {
+  __shared__ int cnt[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (K + 1023) / 1024;
+  const int64_t b = t * per < K ? t * per : K;
+  const int64_t e = b + per < K ? b + per : K;
+  int c = 0;
+  for (int64_t i = b; i < e; ++i) c += mask[i] == 0.0f;
+  cnt[t] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = t >= off ? cnt[t - off] : 0;
+    __syncthreads();
+    cnt[t] += add;
+    __syncthreads();
+  }
+  int64_t p = cnt[t] - c;
+  for (int64_t i = b; i < e; ++i)
+    if (mask[i] == 0.0f) {
+      if (p < n_o) idx[p] = (int32_t)i;
+      ++p;
+    }
 }
 
 template <typename T> __device__ __forceinline__ float gload(const T* p);
@@ -72,11 +113,10 @@ __global__ __launch_bounds__(256) void decomp_gather_kernel(const T* __restrict_
 
 hipError_t launch_decomp_select(const float* absmax, int64_t K, int64_t n_o, int32_t* idx, float* mask,
                                 hipStream_t st) {
-  const dim3 grid((unsigned)((K + 255) / 256)), block(256);
-  hipLaunchKernelGGL(decomp_rank_kernel, grid, block, 0, st, absmax, K, n_o, mask);
+  hipLaunchKernelGGL(decomp_rank_kernel, dim3((unsigned)((K + 63) / 64)), dim3(256), 0, st, absmax, K, n_o, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_o == 0) return e;
-  hipLaunchKernelGGL(decomp_index_kernel, grid, block, 0, st, mask, K, idx);
+  hipLaunchKernelGGL(decomp_index_kernel, dim3(1), dim3(1024), 0, st, mask, K, n_o, idx);
   return hipGetLastError();
 }
 
