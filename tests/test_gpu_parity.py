@@ -44,6 +44,30 @@ def test_col_absmax(sq, dtype, rows, cols):
     assert np.array_equal(host(sq.sq_col_absmax(misaligned(a))), O.col_absmax(A))
 
 
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,N,K", [(1, 3, 8), (37, 300, 1000), (600, 5, 4096), (2050, 1100, 2056), (40, 60, 83)])
+def test_smooth_scales_dtypes(sq, xdt, wdt, T, N, K):
+    """Both column maxima (one fused launch when both operands have 16-byte rows,
+    two launches otherwise) for every dtype pair and uneven T, N."""
+    rng = np.random.default_rng(T + 3 * N + 7 * K)
+    X = (rng.standard_normal((T, K)) * rng.uniform(0.1, 40, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X[T // 2, K // 3] = -900.0
+    W[N - 1, K - 1] = 3.0
+    if xdt == "bf16":
+        X = bf16_round(X)
+    if wdt == "bf16":
+        W = bf16_round(W)
+    Xd, Wd = dev_act(X, xdt), dev_act(W, wdt)
+    s, xa, wa = sq.sq_smooth_scales(Xd, Wd, 0.5)
+    xa_r, wa_r = O.col_absmax(X), O.col_absmax(W)
+    assert np.array_equal(host(xa), xa_r) and np.array_equal(host(wa), wa_r)
+    np.testing.assert_allclose(host(s), O.smooth_scales(xa_r, wa_r, 0.5), rtol=1e-6, atol=0)
+    s2, xa2, wa2 = sq.sq_smooth_scales(misaligned(Xd), Wd, 0.5)     # two-launch path
+    assert np.array_equal(host(xa2), xa_r) and np.array_equal(host(wa2), wa_r)
+
+
 @pytest.mark.parametrize("alpha", [0.0, 0.25, 0.5, 0.75, 1.0])
 def test_smooth_scales(sq, alpha):
     w = WL.page_tiny_fixture(seed=3, T=50, N=70, K=96)

@@ -136,26 +136,26 @@ __global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A
   }
 }
 
-// Column-block form (used for fp32): the 256 threads of a workgroup sit side by
-// side over a block of 256 16-byte column chunks (4 KB of each row) and walk
-// every S-th row (S = gridDim.y, one workgroup per CU in all), U rows of loads in
-// flight, then issue one atomic max per column.  Interleaved rows keep the rows
-// read at any moment by all workgroups one contiguous region of the matrix
-// (8192 x 8192 fp32: 43 us, against 47 us for contiguous row slabs and 55 us for
-// the slab form, whose 4 waves split the rows of short slabs; for bf16 the slab
-// form stays ahead).  Rows past the end repeat the workgroup's previous row
-// (harmless for a maximum), so the loads carry no conditions.
-template <typename T, int VEC, int U>
-__global__ __launch_bounds__(256) void col_absmax_blk_kernel(const T* __restrict__ A, int64_t rows,
-                                                             int64_t cols, float* __restrict__ amax) {
-  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VEC;
+// Column-block form: the 256 threads of a workgroup sit side by side over a
+// block of 256 16-byte column chunks (4 KB of each row) and walk every S-th row
+// starting at row y, U rows of loads in flight, then issue one atomic max per
+// column.  Interleaved rows keep the rows read at any moment by all workgroups
+// one contiguous region of the matrix (8192 x 8192 fp32: 43 us, against 47 us for
+// contiguous row slabs and 55 us for the slab form, whose 4 waves split the rows
+// of short slabs; for bf16 alone the slab form stays ahead).  Rows past the end
+// repeat the workgroup's previous row (harmless for a maximum), so the loads
+// carry no conditions.  Requires S <= rows and 16-byte aligned rows.
+template <typename T, int U>
+__device__ __forceinline__ void colmax_block(const T* __restrict__ A, int64_t rows, int64_t cols, int64_t x,
+                                             int64_t y, int64_t S, float* __restrict__ amax) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t c0 = (x * 256 + threadIdx.x) * VEC;
   if (c0 >= cols) return;   // cols % VEC == 0 on this path
-  const int64_t S = gridDim.y;   // <= rows
   ColMax<T, VEC> acc;
   acc.init();
   const T* p = A + c0;
-  int64_t last = blockIdx.y;
-  for (int64_t r = blockIdx.y; r < rows; r += S * U) {
+  int64_t last = y;
+  for (int64_t r = y; r < rows; r += S * U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t rr = r + u * S;
@@ -167,6 +167,33 @@ __global__ __launch_bounds__(256) void col_absmax_blk_kernel(const T* __restrict
   acc.result(m);
 #pragma unroll
   for (int i = 0; i < VEC; ++i) atomicMax(reinterpret_cast<unsigned int*>(amax + c0 + i), __float_as_uint(m[i]));
+}
+
+// grid (column blocks, S)
+template <typename T, int U>
+__global__ __launch_bounds__(256) void col_absmax_blk_kernel(const T* __restrict__ A, int64_t rows,
+                                                             int64_t cols, float* __restrict__ amax) {
+  colmax_block<T, U>(A, rows, cols, blockIdx.x, blockIdx.y, gridDim.y, amax);
+}
+
+// Both column maxima of the smoothing factors in one launch: workgroups
+// [0, cbX*SX) take the column blocks of X (rows y, y + SX, ...), the others those
+// of W.  SX and SW are chosen so that every workgroup reads about the same
+// bytes, about one workgroup per CU in all; the two streams then share the chip
+// instead of following each other (8192 x 8192 bf16 X and fp32 W: 66 us against
+// 78 us for the two launches).
+template <typename TX, typename TW, int U>
+__global__ __launch_bounds__(256) void col_absmax_pair_kernel(const TX* __restrict__ X, int64_t T, int64_t cbX,
+                                                              int64_t SX, const TW* __restrict__ W, int64_t N,
+                                                              int64_t cbW, int64_t SW, int64_t K,
+                                                              float* __restrict__ xa, float* __restrict__ wa) {
+  const int64_t g = blockIdx.x, nX = cbX * SX;
+  if (g < nX) {
+    colmax_block<TX, U>(X, T, K, g % cbX, g / cbX, SX, xa);
+  } else {
+    const int64_t h = g - nX;
+    colmax_block<TW, U>(W, N, K, h % cbW, h / cbW, SW, wa);
+  }
 }
 
 // Range of the whole smoothed activation tensor, max over t, k of
@@ -329,6 +356,33 @@ static hipError_t col_absmax_t(const T* A, int64_t rows, int64_t cols, float* am
   return hipGetLastError();
 }
 
+template <typename TX, typename TW>
+static hipError_t col_absmax_pair_t(const void* X, int64_t T, const void* W, int64_t N, int64_t K, float* xa,
+                                    float* wa, int ncu, hipStream_t st) {
+  const double bx = (double)T * K * sizeof(TX), bw = (double)N * K * sizeof(TW);
+  const int64_t cbX = (K * (int64_t)sizeof(TX) + 4095) / 4096, cbW = (K * (int64_t)sizeof(TW) + 4095) / 4096;
+  auto interleave = [&](double share, int64_t cb, int64_t rows) {
+    int64_t S = (int64_t)(ncu * share / cb + 0.5);
+    if (S < 1) S = 1;
+    if (S > rows) S = rows;
+    return S;
+  };
+  const int64_t SX = interleave(bx / (bx + bw), cbX, T), SW = interleave(bw / (bx + bw), cbW, N);
+  hipLaunchKernelGGL((col_absmax_pair_kernel<TX, TW, 8>), dim3((unsigned)(cbX * SX + cbW * SW)), dim3(256), 0, st,
+                     static_cast<const TX*>(X), T, cbX, SX, static_cast<const TW*>(W), N, cbW, SW, K, xa, wa);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_absmax_pair(const void* X, bool x_bf16, int64_t T, const void* W, bool w_bf16, int64_t N,
+                                  int64_t K, float* xa, float* wa, int ncu, hipStream_t st) {
+  if (x_bf16) {
+    return w_bf16 ? col_absmax_pair_t<uint16_t, uint16_t>(X, T, W, N, K, xa, wa, ncu, st)
+                  : col_absmax_pair_t<uint16_t, float>(X, T, W, N, K, xa, wa, ncu, st);
+  }
+  return w_bf16 ? col_absmax_pair_t<float, uint16_t>(X, T, W, N, K, xa, wa, ncu, st)
+                : col_absmax_pair_t<float, float>(X, T, W, N, K, xa, wa, ncu, st);
+}
+
 hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, float* amax,
                              bool vec_ok, int ncu, hipStream_t st) {
   if (bf16) {
@@ -343,7 +397,7 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
     if (S < 1) S = 1;
     if (S > rows) S = rows;
     if (S > 65535) S = 65535;
-    hipLaunchKernelGGL((col_absmax_blk_kernel<float, 4, 8>), dim3((unsigned)cb, (unsigned)S), dim3(256), 0,
+    hipLaunchKernelGGL((col_absmax_blk_kernel<float, 8>), dim3((unsigned)cb, (unsigned)S), dim3(256), 0,
                        st, a, rows, cols, amax);
     return hipGetLastError();
   }

@@ -16,6 +16,10 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
 hipError_t launch_fill2(float* p, float* q, int64_t n, float v, hipStream_t st);
 hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t cols, float* amax,
                              bool vec_ok, int ncu, hipStream_t st);
+// Column maxima of X [T][K] and W [N][K] in one launch (running maxima into xa,
+// wa); both with 16-byte aligned rows of a multiple of 16 bytes.
+hipError_t launch_col_absmax_pair(const void* X, bool x_bf16, int64_t T, const void* W, bool w_bf16, int64_t N,
+                                  int64_t K, float* xa, float* wa, int ncu, hipStream_t st);
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
                                 hipStream_t st);
 // Row quantiser modes: per-token activations (divide by s, per-row range),

@@ -136,10 +136,16 @@ sq_status sq_smooth_scales(const void* X, sq_dtype x_t, int64_t T, const void* W
   if (T < 1 || N < 1 || K < 1) return SQ_ERR_SHAPE;
   if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
   if (sq::launch_fill2(x_absmax, w_absmax, K, 0.0f, stream) != hipSuccess) return SQ_ERR_HIP;
-  sq_status r = sq_col_absmax(X, x_t, T, K, x_absmax, 1, stream);
-  if (r != SQ_OK) return r;
-  r = sq_col_absmax(W, w_t, N, K, w_absmax, 1, stream);
-  if (r != SQ_OK) return r;
+  if (rows_vec16(X, K, esize(x_t)) && rows_vec16(W, K, esize(w_t))) {
+    if (sq::launch_col_absmax_pair(X, x_t == SQ_BF16, T, W, w_t == SQ_BF16, N, K, x_absmax, w_absmax, cu_count(),
+                                   stream) != hipSuccess)
+      return SQ_ERR_HIP;
+  } else {
+    sq_status r = sq_col_absmax(X, x_t, T, K, x_absmax, 1, stream);
+    if (r != SQ_OK) return r;
+    r = sq_col_absmax(W, w_t, N, K, w_absmax, 1, stream);
+    if (r != SQ_OK) return r;
+  }
   return sq_smooth_scales_from_absmax(x_absmax, w_absmax, K, alpha, s, stream);
 }
 
