@@ -40,6 +40,64 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 
 }  // namespace
 
+// so[i][b][e] = sum over o ascending of xo[o][t] * wo[o][n] for the lane's token
+// t = b*16 + fi and channel n = n0 + i*16 + 4*fg + e, channel blocks I0 <= i < I1;
+// one binary32 rounding per multiply and per add.  Each step reads the lane's
+// token values and channel quadruples once (from the LDS copies ox [n_o][TB*16]
+// and ow [n_o][NB*16] when staged, else from xo / wo) and advances all the sums.
+// Entries past T or N are zero and never stored.
+template <int NB, int TB, int I0, int I1>
+__device__ __forceinline__ void gemv_outlier_sums(float (&so)[NB][TB][4], int n_o, int stage,
+                                                  const float* ox, const float* ow, const float* __restrict__ xo,
+                                                  int64_t ldxo, const float* __restrict__ wo, int64_t ldwo, int T,
+                                                  int N, int n0, int fi, int fg) {
+  constexpr int TL = TB * 16, CL = NB * 16;
+  // operands of outlier o: token values xb[b], channel quadruples wi[i][e]
+  auto fetch = [&](int o, float* xb, float (*wi)[4]) {
+    if (stage) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b) xb[b] = ox[o * TL + b * 16 + fi];
+#pragma unroll
+      for (int i = I0; i < I1; ++i) {
+        const float4 w4 = *reinterpret_cast<const float4*>(ow + o * CL + i * 16 + 4 * fg);
+        wi[i][0] = w4.x; wi[i][1] = w4.y; wi[i][2] = w4.z; wi[i][3] = w4.w;
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < TB; ++b) xb[b] = b * 16 + fi < T ? xo[(int64_t)o * ldxo + b * 16 + fi] : 0.0f;
+#pragma unroll
+      for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + i * 16 + 4 * fg + e;
+          wi[i][e] = n < N ? wo[(int64_t)o * ldwo + n] : 0.0f;
+        }
+    }
+  };
+  auto step = [&](const float* xb, const float (*wi)[4]) {
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) so[i][b][e] = so[i][b][e] + xb[b] * wi[i][e];
+  };
+  // four outliers' operands are fetched before their four steps (in order)
+  int o = 0;
+  for (; o + 4 <= n_o; o += 4) {
+    float xb[4][TB], wi[4][NB][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fetch(o + u, xb[u], wi[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) step(xb[u], wi[u]);
+  }
+  for (; o < n_o; ++o) {
+    float xb[TB], wi[NB][4];
+    fetch(o, xb, wi);
+    step(xb, wi);
+  }
+}
+
 // Requires K % 16 == 0, N * K < 2^31 and T * K < 2^31 (the host splits larger N),
 // 16-byte aligned Xq and Wq.  KW waves per workgroup, which owns NB*16 channels.
 // OUTL: the epilogue adds the binary32 outlier-channel product of the
@@ -48,7 +106,8 @@ template <int NB, int TB, int OUT, int KW, bool OUTL>
 __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy, int vec_store,
-    const float* __restrict__ xo, int64_t ldxo, const float* __restrict__ wo, int64_t ldwo, int n_o) {
+    const float* __restrict__ xo, int64_t ldxo, const float* __restrict__ wo, int64_t ldwo, int n_o,
+    int stage) {
   // The body exists only in the device pass (the host pass needs just the stub).
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = 256;                 // K bytes per chunk
@@ -59,7 +118,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
   constexpr int KS = KC / 64;             // MFMA k-steps per chunk (4)
   constexpr int kOob = 0x7FFFFFF0;        // offset the range check turns into zeros
   __shared__ __attribute__((aligned(1024))) int8_t lds_all[KW][16 * NB * KC];
-  static_assert((KW - 1) * NB * TB * 64 * 16 <= KW * 16 * NB * KC, "partial sums must fit the LDS tiles");
+  static_assert(KW * NB * TB * 64 * 16 <= KW * 16 * NB * KC, "partial and outlier sums must fit the LDS tiles");
+  static_assert(!OUTL || KW <= 2, "the outlier sums are split between at most two waves");
   const int lane = threadIdx.x & 63, kw = threadIdx.x >> 6;
   int8_t* lds = lds_all[kw];   // this wave's transpose tile
   const int n0 = blockIdx.x * 16 * NB;
@@ -141,9 +201,55 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
   // this wave's chunks: kw, kw + KW, kw + 2 KW, ...
   const int nall = (K + KC - 1) / KC;
   const int nit = nall > kw ? (nall - kw + KW - 1) / KW : 0;
+  // Outlier operands of this workgroup's outputs (stage != 0): the token values
+  // xo[o][t < TB*16] and the channel values wo[o][n0 .. n0 + 16 NB) are copied into
+  // LDS, 32 independent loads per thread at a time, so the epilogue reads them
+  // from LDS.  The first batch is loaded before the first weight chunk is issued
+  // and stored after it, so that its round trip overlaps the chunk's.
+  constexpr int TL = TB * 16, CL = NB * 16;
+  extern __shared__ __attribute__((aligned(16))) float gemv_outl[];
+  float* ox = gemv_outl;             // [n_o][TL]
+  float* ow = gemv_outl + n_o * TL;  // [n_o][CL]
+  const int nx = n_o * TL, ntot = nx + n_o * CL;
+  auto stage_load = [&](int q) {
+    float v = 0.0f;
+    if (q < nx) {
+      const int o = q / TL, tl = q - o * TL;
+      if (tl < T) v = xo[(int64_t)o * ldxo + tl];
+    } else if (q < ntot) {
+      const int o = (q - nx) / CL, c = q - nx - o * CL;
+      if (n0 + c < N) v = wo[(int64_t)o * ldwo + n0 + c];
+    }
+    return v;
+  };
+  constexpr int SB = 32, SSTEP = SB * 64 * KW;   // loads per thread per batch, entries per batch
+  float sv[SB];
+  if (OUTL && stage) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) sv[u] = stage_load(threadIdx.x + u * 64 * KW);
+  }
+
   static_for(std::make_integer_sequence<int, D - 1>{}, [&](auto u) {
     if (decltype(u)::value < nit) load(u, (decltype(u)::value * KW + kw) * KC);
   });
+
+  if (OUTL && stage) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int q = threadIdx.x + u * 64 * KW;
+      if (q < ntot) gemv_outl[q] = sv[u];
+    }
+    for (int q0 = threadIdx.x + SSTEP; q0 < ntot; q0 += SSTEP) {
+#pragma unroll
+      for (int u = 0; u < SB; ++u) sv[u] = stage_load(q0 + u * 64 * KW);
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int q = q0 + u * 64 * KW;
+        if (q < ntot) gemv_outl[q] = sv[u];
+      }
+    }
+  }
+
   for (int q0 = 0; q0 < nit; q0 += D) {
     static_for(std::make_integer_sequence<int, D>{}, [&](auto u) {
       constexpr int uu = decltype(u)::value;
@@ -152,16 +258,46 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
       if (q < nit) compute(u);
     });
   }
+  // Outlier-channel products of this lane's outputs (gemv_outlier_sums).  With
+  // two waves, wave 0 forms the sums of channel blocks i < NB/2 and wave 1 those
+  // of the others, at the same time; each sum is formed by one wave.
+  float so[NB][TB][4];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) so[i][b][e] = 0.0f;
+  auto outlier_sums = [&]() {
+    if (KW == 1)
+      gemv_outlier_sums<NB, TB, 0, NB>(so, n_o, stage, ox, ow, xo, ldxo, wo, ldwo, T, N, n0, fi, fg);
+    else if (kw == 0)
+      gemv_outlier_sums<NB, TB, 0, NB / 2>(so, n_o, stage, ox, ow, xo, ldxo, wo, ldwo, T, N, n0, fi, fg);
+    else
+      gemv_outlier_sums<NB, TB, NB / 2, NB>(so, n_o, stage, ox, ow, xo, ldxo, wo, ldwo, T, N, n0, fi, fg);
+  };
+
   if (KW > 1) {
     // exact integer sum of the KW partial accumulators; the LDS tiles are free
     // once every wave has passed the first barrier
     __syncthreads();
     v4i* red = reinterpret_cast<v4i*>(&lds_all[0][0]);
+    float4* sor = reinterpret_cast<float4*>(red + (KW - 1) * NB * TB * 64);
     if (kw > 0) {
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int b = 0; b < TB; ++b) red[((kw - 1) * NB * TB + i * TB + b) * 64 + lane] = acc[i][b];
+    }
+    if (OUTL) {
+      outlier_sums();
+      if (kw == 1) {
+#pragma unroll
+        for (int i = NB / 2; i < NB; ++i)
+#pragma unroll
+          for (int b = 0; b < TB; ++b)
+            sor[(i * TB + b) * 64 + lane] = make_float4(so[i][b][0], so[i][b][1], so[i][b][2], so[i][b][3]);
+      }
     }
     __syncthreads();
     if (kw > 0) return;
@@ -171,6 +307,18 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
       for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int b = 0; b < TB; ++b) acc[i][b] += red[((w - 1) * NB * TB + i * TB + b) * 64 + lane];
+    if (OUTL) {
+#pragma unroll
+      for (int i = NB / 2; i < NB; ++i)
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          const float4 f = sor[(i * TB + b) * 64 + lane];
+          so[i][b][0] = f.x; so[i][b][1] = f.y; so[i][b][2] = f.z; so[i][b][3] = f.w;
+        }
+    }
+  } else if (OUTL) {
+    if (stage) __syncthreads();
+    outlier_sums();
   }
 
   // epilogue: lane holds n = n0 + i*16 + 4*fg + 0..3 for token t = b*16 + fi
@@ -194,33 +342,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (sc * wsv[i][e]) : 0.0f;
       if (OUTL) {
-        // binary32 outlier-channel product, o ascending; loads 8 outliers ahead
-        float so[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int o0 = 0; o0 < n_o; o0 += 8) {
-          float xv[8], wv[8][4];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const bool in = o0 + u < n_o;
-            const int64_t ro = (int64_t)(o0 + u);
-            xv[u] = in ? xo[ro * ldxo + t] : 0.0f;
-            if (in && vec) {
-              const float4 w4 = *reinterpret_cast<const float4*>(wo + ro * ldwo + n);
-              wv[u][0] = w4.x; wv[u][1] = w4.y; wv[u][2] = w4.z; wv[u][3] = w4.w;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) wv[u][e] = (in && e < nrem) ? wo[ro * ldwo + n + e] : 0.0f;
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (o0 + u < n_o) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (e < nrem) so[e] = so[e] + xv[u] * wv[u][e];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = v[e] + so[e];
+        for (int e = 0; e < 4; ++e) v[e] = v[e] + so[i][b][e];
       }
       if (OUT == kOutF32) {
         float* y = static_cast<float*>(Y) + (int64_t)t * ldy + n;
@@ -241,6 +364,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 #endif
 }
 
+constexpr size_t kGemvOutlierLds = 64 * 1024;
+
 template <int NB, int TB>
 static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int KW = 2;
@@ -259,9 +384,13 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
     const bool outl = a.n_o > 0 && a.out != kOutI32;
     const float* wo = outl ? a.wo + nb : nullptr;
     const int n_o = outl ? (int)a.n_o : 0;
-#define SQ_GEMV_LAUNCH(O, L)                                                                           \
-  hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, O, KW, L>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, \
-                     a.N, vs, a.xo, a.T, wo, a.N, n_o)
+    // outlier operands staged in LDS up to 64 KB per workgroup
+    const size_t dyn = (size_t)n_o * 16 * (TB + NB) * sizeof(float);
+    const int stage = (outl && dyn <= kGemvOutlierLds) ? 1 : 0;
+    const size_t shm = stage ? dyn : 0;
+#define SQ_GEMV_LAUNCH(O, L)                                                                             \
+  hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, O, KW, L>), grid, block, shm, st, a.Xq, a.xs, Wq, ws, T, N, K, \
+                     Y, a.N, vs, a.xo, a.T, wo, a.N, n_o, stage)
     switch (a.out) {
       case kOutF32:
         if (outl) SQ_GEMV_LAUNCH(kOutF32, true); else SQ_GEMV_LAUNCH(kOutF32, false);
