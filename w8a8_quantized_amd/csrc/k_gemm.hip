@@ -381,6 +381,36 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     constexpr int RPI = 64 / CPRO;             // output rows per wave instruction
     static_assert(NW * 32 * ROWB <= STAGES * STAGE_BYTES, "epilogue staging does not fit");
     int8_t* E = lds + wave * (32 * ROWB);
+    // Outlier operands of this tile (decomposition): the token values
+    // xo[o][t0 .. t0 + BT) and channel values wo[o][n0 .. n0 + BN) are copied
+    // into the LDS past the staging rows when they fit (zero past T or N), so
+    // the epilogue reads them from LDS; else it reads them from xo / wo.
+    constexpr int OFREE = STAGES * STAGE_BYTES - NW * 32 * ROWB;
+    float* oxl = reinterpret_cast<float*>(lds + NW * 32 * ROWB);   // [n_o][BT]
+    float* owl = oxl + (OUTL ? n_o : 0) * BT;                       // [n_o][BN]
+    const bool ostage = OUTL && n_o > 0 && n_o * (BT + BN) * 4 <= OFREE;
+    if (ostage) {
+      const int nx = n_o * BT, ntot = nx + n_o * BN;
+      for (int q0 = threadIdx.x; q0 < ntot; q0 += 4 * NW * 64) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u * NW * 64;
+          v[u] = 0.0f;
+          if (q < nx) {
+            const int o = q / BT, tt = q - o * BT;
+            if (t0 + tt < T) v[u] = xo[(int64_t)o * ldxo + t0 + tt];
+          } else if (q < ntot) {
+            const int o = (q - nx) / BN, nn = q - nx - o * BN;
+            if (n0 + nn < N) v[u] = wo[(int64_t)o * ldwo + n0 + nn];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (q0 + u * NW * 64 < ntot) oxl[q0 + u * NW * 64] = v[u];
+      }
+      __syncthreads();
+    }
     // channel scales held across the token blocks (re-read per block instead
     // when the outlier term needs the registers)
     float wsq[RN][4][4];
@@ -403,7 +433,31 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
         // LDS accesses of one wave complete in order, so this round's writes
         // follow the previous round's reads of the same staging rows.
 #pragma unroll
-        for (int i = ib; i < ib + EI; ++i)
+        for (int i = ib; i < ib + EI; ++i) {
+          // staged outlier sums of this lane's four channel quadruples of block
+          // i for token t_l: one pass over the outliers in ascending order, one
+          // binary32 rounding per multiply and per add
+          float so4[4][4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) so4[g][e] = 0.0f;
+          if (OUTL && ostage) {
+            const int tt = t_l - t0, nn = wn * WTN + i * 32 + 4 * fc;
+            for (int o = 0; o < n_o; ++o) {
+              const float x = oxl[o * BT + tt];
+              float4 w4[4];
+#pragma unroll
+              for (int g = 0; g < 4; ++g) w4[g] = *reinterpret_cast<const float4*>(owl + o * BN + nn + 8 * g);
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                so4[g][0] = so4[g][0] + x * w4[g].x;
+                so4[g][1] = so4[g][1] + x * w4[g].y;
+                so4[g][2] = so4[g][2] + x * w4[g].z;
+                so4[g][3] = so4[g][3] + x * w4[g].w;
+              }
+            }
+          }
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             int8_t* dst = E + fr * ROWB + ((i - ib) * 32 + 8 * g + 4 * fc) * OB;
@@ -422,9 +476,9 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
               }
               if (OUTL) {
                 const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * fc;
-                float so[4] = {0.f, 0.f, 0.f, 0.f};
-                // chunks of 4 keep the 16-wave tile within its 128 registers
-                if (t_l < T && n < N) outlier_sum4<(NW > 8 ? 4 : 8)>(xo + t_l, ldxo, wo + n, ldwo, n_o, so);
+                float so[4] = {so4[g][0], so4[g][1], so4[g][2], so4[g][3]};
+                // unstaged: chunks of 4 keep the 16-wave tile within its 128 registers
+                if (!ostage && t_l < T && n < N) outlier_sum4<(NW > 8 ? 4 : 8)>(xo + t_l, ldxo, wo + n, ldwo, n_o, so);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = v[e] + so[e];
               }
@@ -438,6 +492,7 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
               }
             }
           }
+        }
 #pragma unroll
         for (int it = 0; it < 32 / RPI; ++it) {
           const int row = it * RPI + lane / CPRO, ch = lane % CPRO;
