@@ -92,6 +92,27 @@ def test_decomp_layer(sq, xdt, T, N, K, n_o, out):
         _check_split(host(Xq2), host(xs2), host(Xo2), Xq_r, xs_r, Xo_r, idx_h)
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("T,N,K,n_o", [(100, 96, 512, 90), (100, 96, 512, 110), (2048, 2048, 256, 120),
+                                       (4096, 4096, 128, 26), (4096, 4096, 128, 30)])
+def test_decomp_gemm_outlier_staging(sq, T, N, K, n_o, out):
+    """Prefill tiles copy their outlier operands into LDS when they fit (64x64
+    tiles up to ~90 outliers, 128x128 up to ~94-107, 256x256 up to 26) and read
+    them from global memory otherwise: outlier counts on both sides of those
+    limits, outputs in full."""
+    rng = np.random.default_rng(T + N + K + n_o)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    X[:, rng.choice(K, n_o, replace=False)] *= 25
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    idx, mask, Wq, ws, Wo = _prep_gpu(sq, X, "f32", W, n_o)
+    idx_h = host(idx)
+    Wq_r, ws_r, Wo_r = O.decomp_prepare(W, idx_h)
+    Xq, xs, Xo = sq.sq_decomp_quant_act(dev_act(X, "f32"), mask, idx)
+    y_r, *_ = O.decomp_linear(X, idx_h, Wq_r, ws_r, Wo_r)
+    y = sq.sq_decomp_gemm(Xq, xs, Wq, ws, Xo, Wo, out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    assert_out_close(host(y), y_r, out)
+
+
 def test_decomp_generic_gemm_path(sq):
     """Misaligned int8 operands take the one-output-per-thread kernel."""
     rng = np.random.default_rng(5)
