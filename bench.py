@@ -83,7 +83,7 @@ def _omp_threads():
         return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
-def cpu_baseline(w, target_s=15.0):
+def cpu_baseline(w, target_s=20.0):
     """The oracle as it stands, on a prefix of the workload's tokens: statistics,
     smoothing factors and weight quantisation in full, then quantisation, integer
     GEMM, epilogue and bf16 rounding for `tokens` tokens.  Throughput in TOPS of
