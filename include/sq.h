@@ -28,6 +28,9 @@
  *   - Work is enqueued on `stream` (0 = the null stream) and runs
  *     asynchronously; no call synchronises the stream or allocates device
  *     memory.  Outputs are valid once the stream reaches the enqueued work.
+ *     Buffers that accumulate are cleared by kernels, not by memory-set
+ *     commands, so a sequence of calls can be captured in a HIP graph and
+ *     replayed (the graph replays the same pointers and sizes).
  *   - Arguments are validated on the host before anything is enqueued.  On any
  *     error other than SQ_ERR_HIP nothing is launched and no output is written.
  *     SQ_ERR_HIP means a kernel launch was rejected by the HIP runtime; outputs
