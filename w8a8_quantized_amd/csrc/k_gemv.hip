@@ -9,10 +9,13 @@
 //   * loads run D chunks ahead in a register ring, so several chunks per wave are
 //     in flight;
 //   * a workgroup owns NB*16 output channels; its KW waves take alternate K
-//     chunks (more loads in flight than one wave per channel block: KW = 2 measured
-//     4-5% faster than 1, and 4 slower), then add their int32 partial sums exactly
-//     through LDS; each wave re-reads the small activation codes (L2-resident) once
-//     per chunk for all of its channels.
+//     chunks (KW = 2 measured equal to or up to ~2% faster than 1 depending on the
+//     GPU, 4 clearly slower), then add their int32 partial sums exactly through
+//     LDS; each wave re-reads the small activation codes (L2-resident) once per
+//     chunk for all of its channels;
+//   * the epilogue's scale factors, and the decomposition's outlier operands
+//     (copied into LDS), are fetched before the K loop, so no memory round trip
+//     is left for the end of a workgroup.
 // v_mfma_i32_16x16x64_i8 wants a 16-row block of Wq with lane l holding 16 bytes
 // of row l%16, so each chunk is transposed through a per-wave LDS tile: rows are
 // written as loaded and read back in the MFMA layout, with the 16-byte chunk
