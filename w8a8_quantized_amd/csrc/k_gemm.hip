@@ -150,13 +150,18 @@ constexpr int kLgkm0 = ~0x0F00;
 // and Mixed-Precision Decomposition", section "Decomposition"): the float
 // epilogue value gets the binary32 product of the outlier channels added,
 //   y = fl32(fl32(acc) * fl32(xs * ws)) + (sum over o ascending of xo[o][t] * wo[o][n]).
+// When they fit in the freed operand ring, the tile's outlier operands are first
+// copied into LDS, and each lane forms the sums of a 32-channel block's four
+// channel quadruples in one pass over the outliers; otherwise it reads xo / wo
+// from global memory per quadruple.
 //
 // F8 (FP8 E4M3 operands, inferenceinterviews.com formats paragraph): the same
 // byte tiles feed v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) with
 // binary32 accumulators.  One MFMA takes, per lane, the two 16-byte chunks that
 // two consecutive int8 k-steps would take, for A and B alike, so every product
 // pairs the same k.  Fragments are read straight into the 8-register operands,
-// one step at a time (the 16-wave tile has no registers for a second set).
+// one step at a time; FP8 runs 8 waves of 64x128 per 256x256 tile (the operands
+// are twice as wide per lane, and the 16-wave layout would spill).
 template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC, bool OUTL, bool F8>
 __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
