@@ -38,7 +38,9 @@ def _case(seed, T, K, N, dtype):
     return X, W, s
 
 
-SHAPES = [(1, 8, 16), (16, 300, 512), (70, 200, 1040), (300, 520, 2048), (33, 64, 133), (257, 264, 4096)]
+# T <= 64 with K % 16 == 0 takes the decode kernel (16, 32 or 64 tokens per block)
+SHAPES = [(1, 8, 16), (16, 300, 512), (70, 200, 1040), (300, 520, 2048), (33, 64, 133), (257, 264, 4096),
+          (24, 100, 2048), (64, 264, 1024), (5, 72, 8208)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -118,7 +120,8 @@ def test_fp8_gemm_misaligned_generic(sq):
     assert np.all(np.abs(y[ti, ni] - exact * sc) <= 64 * 2.0 ** -24 * sab * sc + 2.0 ** -23 * np.abs(exact * sc))
 
 
-@pytest.mark.parametrize("name", ["heavy_t8192_k8192_n8192", "prefill_t2048_k4096_n16384"])
+@pytest.mark.parametrize("name", ["heavy_t8192_k8192_n8192", "prefill_t2048_k4096_n16384",
+                                  "decode_t16_k8192_n28672"])
 def test_fp8_full_size(sq, name):
     """The workload's smoothed operands in FP8: all codes and scales; the GEMM on
     sampled (t, n) pairs against exact dot products."""

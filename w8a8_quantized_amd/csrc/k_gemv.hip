@@ -30,6 +30,8 @@
 
 namespace sq {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 namespace {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int bytes) {
@@ -103,9 +105,13 @@ __device__ __forceinline__ void gemv_outlier_sums(float (&so)[NB][TB][4], int n_
 
 // Requires K % 16 == 0, N * K < 2^31 and T * K < 2^31 (the host splits larger N),
 // 16-byte aligned Xq and Wq.  KW waves per workgroup, which owns NB*16 channels.
+// F8: the codes are FP8 E4M3 and each pair of 64-byte k-steps is one
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales, binary32 accumulators):
+// a lane joins the two 16-byte chunks it would take for the two int8 steps, for
+// the weights and the token codes alike, so every product pairs the same k.
 // OUTL: the epilogue adds the binary32 outlier-channel product of the
 // mixed-precision decomposition, sum over o ascending of xo[o][t] * wo[o][n].
-template <int NB, int TB, int OUT, int KW, bool OUTL>
+template <int NB, int TB, int OUT, int KW, bool OUTL, bool F8>
 __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ xs, const int8_t* __restrict__ Wq,
     const float* __restrict__ ws, int T, int N, int K, void* __restrict__ Y, int64_t ldy, int vec_store,
@@ -164,11 +170,13 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
         if (n0 + i * 16 + 4 * fg + e < N) wsv[i][e] = ws[n0 + i * 16 + 4 * fg + e];
   }
 
-  v4i acc[NB][TB];
+  static_assert(!(F8 && (OUTL || OUT == kOutI32)), "FP8: float outputs, no outlier term");
+  using AccT = std::conditional_t<F8, v4f, v4i>;
+  AccT acc[NB][TB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int b = 0; b < TB; ++b) acc[i][b] = v4i{0, 0, 0, 0};
+    for (int b = 0; b < TB; ++b) acc[i][b] = AccT{0, 0, 0, 0};
 
   v4i wr[D][NI], xv[D][TB][KS];
   auto load = [&](auto slot_c, int k0) {
@@ -188,15 +196,33 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
     constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int p = 0; p < NI; ++p) *reinterpret_cast<v4i*>(lds + w_lds[p]) = wr[sl][p];
+    if constexpr (F8) {
 #pragma unroll
-    for (int m = 0; m < KS; ++m) {
-      const int c = m * 4 + fg;
+      for (int m = 0; m < KS; m += 2) {
+        const int c0 = m * 4 + fg, c1 = c0 + 4;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const v4i wv = *reinterpret_cast<const v4i*>(lds + (i * 16 + fi) * KC + ((c ^ fi) * 16));
+        for (int i = 0; i < NB; ++i) {
+          const v8i wv = __builtin_shufflevector(
+              *reinterpret_cast<const v4i*>(lds + (i * 16 + fi) * KC + ((c0 ^ fi) * 16)),
+              *reinterpret_cast<const v4i*>(lds + (i * 16 + fi) * KC + ((c1 ^ fi) * 16)), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int b = 0; b < TB; ++b)
-          acc[i][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, xv[sl][b][m], acc[i][b], 0, 0, 0);
+          for (int b = 0; b < TB; ++b) {
+            const v8i x8 = __builtin_shufflevector(xv[sl][b][m], xv[sl][b][m + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, x8, acc[i][b], 0, 0, 0, 127, 0, 127);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        const int c = m * 4 + fg;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const v4i wv = *reinterpret_cast<const v4i*>(lds + (i * 16 + fi) * KC + ((c ^ fi) * 16));
+#pragma unroll
+          for (int b = 0; b < TB; ++b)
+            acc[i][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, xv[sl][b][m], acc[i][b], 0, 0, 0);
+        }
       }
     }
   };
@@ -284,7 +310,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
     // exact integer sum of the KW partial accumulators; the LDS tiles are free
     // once every wave has passed the first barrier
     __syncthreads();
-    v4i* red = reinterpret_cast<v4i*>(&lds_all[0][0]);
+    AccT* red = reinterpret_cast<AccT*>(&lds_all[0][0]);
     float4* sor = reinterpret_cast<float4*>(red + (KW - 1) * NB * TB * 64);
     if (kw > 0) {
 #pragma unroll
@@ -333,7 +359,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
       if (t >= T || n >= N) continue;
       const int nrem = N - n;
       const bool vec = vec_store && nrem >= 4;
-      const v4i a4 = acc[i][b];
+      const AccT a4 = acc[i][b];
       if (OUT == kOutI32) {
         int* y = static_cast<int*>(Y) + (int64_t)t * ldy + n;
         if (vec) *reinterpret_cast<int4*>(y) = make_int4(a4[0], a4[1], a4[2], a4[3]);
@@ -369,7 +395,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 
 constexpr size_t kGemvOutlierLds = 64 * 1024;
 
-template <int NB, int TB>
+template <int NB, int TB, bool F8>
 static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int KW = 2;
   // split N so that one launch's weight slice spans < 2^31 bytes (32-bit offsets)
@@ -392,18 +418,22 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
     const int stage = (outl && dyn <= kGemvOutlierLds) ? 1 : 0;
     const size_t shm = stage ? dyn : 0;
 #define SQ_GEMV_LAUNCH(O, L)                                                                             \
-  hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, O, KW, L>), grid, block, shm, st, a.Xq, a.xs, Wq, ws, T, N, K, \
-                     Y, a.N, vs, a.xo, a.T, wo, a.N, n_o, stage)
-    switch (a.out) {
-      case kOutF32:
-        if (outl) SQ_GEMV_LAUNCH(kOutF32, true); else SQ_GEMV_LAUNCH(kOutF32, false);
-        break;
-      case kOutBF16:
-        if (outl) SQ_GEMV_LAUNCH(kOutBF16, true); else SQ_GEMV_LAUNCH(kOutBF16, false);
-        break;
-      default:
-        SQ_GEMV_LAUNCH(kOutI32, false);
-        break;
+  hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, O, KW, L, F8>), grid, block, shm, st, a.Xq, a.xs, Wq, ws, T, N, \
+                     K, Y, a.N, vs, a.xo, a.T, wo, a.N, n_o, stage)
+    if constexpr (F8) {   // float outputs only (the ABI rejects int32 for FP8)
+      if (a.out == kOutF32) SQ_GEMV_LAUNCH(kOutF32, false); else SQ_GEMV_LAUNCH(kOutBF16, false);
+    } else {
+      switch (a.out) {
+        case kOutF32:
+          if (outl) SQ_GEMV_LAUNCH(kOutF32, true); else SQ_GEMV_LAUNCH(kOutF32, false);
+          break;
+        case kOutBF16:
+          if (outl) SQ_GEMV_LAUNCH(kOutBF16, true); else SQ_GEMV_LAUNCH(kOutBF16, false);
+          break;
+        default:
+          SQ_GEMV_LAUNCH(kOutI32, false);
+          break;
+      }
     }
 #undef SQ_GEMV_LAUNCH
     hipError_t e = hipGetLastError();
@@ -414,9 +444,14 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   (void)ncu;
-  if (a.T <= 16) return gemv_cfg<4, 1>(a, st);
-  if (a.T <= 32) return gemv_cfg<2, 2>(a, st);
-  return gemv_cfg<2, 4>(a, st);
+  if (a.f8) {
+    if (a.T <= 16) return gemv_cfg<4, 1, true>(a, st);
+    if (a.T <= 32) return gemv_cfg<2, 2, true>(a, st);
+    return gemv_cfg<2, 4, true>(a, st);
+  }
+  if (a.T <= 16) return gemv_cfg<4, 1, false>(a, st);
+  if (a.T <= 32) return gemv_cfg<2, 2, false>(a, st);
+  return gemv_cfg<2, 4, false>(a, st);
 }
 
 }  // namespace sq
