@@ -132,26 +132,35 @@ def decode_measure(sq, torch, reps=30):
     Xc = torch.from_numpy(w.X_calib).to(torch.bfloat16).to(dev)
     s, _, _ = sq.sq_smooth_scales(Xc, W, w.alpha)
     Wq, ws = sq.sq_quantize_weights(W, s)
+    Wq8, ws8 = sq.sq_quantize_weights_fp8(W, s)
     del W
     torch.cuda.empty_cache()    # each copy in an allocation of its own
     copies = [Wq] + [Wq.clone() for _ in range(2)]
+    copies8 = [Wq8] + [Wq8.clone() for _ in range(2)]
     Xq, xs = sq.sq_quant_act(X, s)
+    Xq8, xs8 = sq.sq_quant_act_fp8(X, s)
     Y = torch.empty((w.T, w.N), dtype=torch.bfloat16, device=dev)
-    for i in range(6):
-        sq.sq_w8a8_gemm(Xq, xs, copies[i % 3], ws, Y=Y)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(20_000_000)   # keeps the GPU busy while the launches are queued
-    a.record()
-    for i in range(reps):
-        sq.sq_w8a8_gemm(Xq, xs, copies[i % 3], ws, Y=Y)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+
+    def per_launch(fn, cps):
+        for i in range(6):
+            fn(cps[i % 3])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)   # keeps the GPU busy while the launches are queued
+        a.record()
+        for i in range(reps):
+            fn(cps[i % 3])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms = per_launch(lambda wq: sq.sq_w8a8_gemm(Xq, xs, wq, ws, Y=Y), copies)
+    ms8 = per_launch(lambda wq: sq.sq_fp8_gemm(Xq8, xs8, wq, ws8, Y=Y), copies8)
     byts = _gemm_bytes(w.T, w.N, w.K, 2)
-    gbs = byts / (ms * 1e-3) / 1e9
+    gbs, gbs8 = byts / (ms * 1e-3) / 1e9, byts / (ms8 * 1e-3) / 1e9
     return {"workload": w.name, "T": w.T, "N": w.N, "K": w.K, "us": ms * 1e3, "GB/s": gbs,
-            "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": byts, "weight_copies_rotated": 3}
+            "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": byts, "weight_copies_rotated": 3,
+            "fp8": {"us": ms8 * 1e3, "GB/s": gbs8, "frac_hbm": gbs8 / PEAK_HBM_GBS}}
 
 
 def _time_calls(torch, fn, copies, reps=20):
