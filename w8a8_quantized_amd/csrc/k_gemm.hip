@@ -127,7 +127,7 @@ __device__ __forceinline__ void tile_coords(int bid, int G, int tiles_n, int til
 // s_waitcnt immediate for "vmcnt <= n" (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14; expcnt 6:4 left at 7; lgkmcnt 11:8 at 15, or at 0 with kLgkm0).
 constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
-constexpr int kLgkm0 = ~0x0F00;
+[[maybe_unused]] constexpr int kLgkm0 = ~0x0F00;
 
 // Requires K % 16 == 0, (N + BN) * K < 2^31 and (T + BT) * K < 2^31 (the host
 // splits larger problems), 16-byte aligned Xq and Wq.

@@ -34,7 +34,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 namespace {
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int bytes) {
+[[maybe_unused]] __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
