@@ -686,17 +686,19 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // 256x256 tiles when they fill the chip at least once; the big tile runs 16
   // waves of 64x64 (4 per SIMD): with fewer, larger wave tiles the per-stage
   // barrier and LDS latency are not covered (measured ~8% slower).  Smaller
-  // problems are latency-bound: 128x128 tiles, else 64x64 tiles, both with a
-  // 4-deep ring (two workgroups per CU for 64x64): 512x4096x4096 18.2 us and
-  // 128x1024x1024 5.5 us, against 25.8 and 8.4 us with 128x128 and 2 stages.
+  // problems are latency-bound: 128x128 tiles, else 64x64 tiles (two workgroups
+  // per CU), both with two 256-byte K stages, which halve the stage count
+  // against 128-byte stages in a 4-deep ring of the same LDS size:
+  // 512x4096x4096 17.7 us, 1024x4096x4096 26.3 us and 128x1024x1024 5.2 us,
+  // against 19.1, 28.3 and 5.6 us.
   // More 256x256 tiles than CUs: the persistent form (one workgroup per CU
   // walks its tiles and streams the next tile's first stage during the
   // epilogue; measured 2-3% faster on 8192^3 and 2048x16384x4096).
   const int64_t big = ((a.N + 255) / 256) * ((a.T + 255) / 256);
   if (big >= ncu) return gemm_cfg<256, 256, 128, 4, 4, 2, false, true>(a, st, ncu);
   const int64_t mid = ((a.N + 127) / 128) * ((a.T + 127) / 128);
-  if (mid >= ncu) return gemm_cfg<128, 128, 128, 2, 2, 4>(a, st);
-  return gemm_cfg<64, 64, 128, 2, 2, 4>(a, st);
+  if (mid >= ncu) return gemm_cfg<128, 128, 256, 2, 2, 2>(a, st);
+  return gemm_cfg<64, 64, 256, 2, 2, 2>(a, st);
 }
 
 // ---------------------------------------------------------------- generic path
