@@ -167,9 +167,12 @@ constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 1
 // byte tiles feed v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) with
 // binary32 accumulators.  One MFMA takes, per lane, the two 16-byte chunks that
 // two consecutive int8 k-steps would take, for A and B alike, so every product
-// pairs the same k.  Fragments are read straight into the 8-register operands,
-// one step at a time; FP8 runs 8 waves of 64x128 per 256x256 tile (the operands
-// are twice as wide per lane, and the 16-wave layout would spill).
+// pairs the same k.  FP8 runs 8 waves of 64x128 per 256x256 tile (the operands
+// are twice as wide per lane, and the 16-wave layout would spill); the A
+// fragments alternate between two register slots and each B fragment is re-read
+// for the next step once its last MFMA of the step has issued, so the reads
+// overlap the MFMAs within the 256 registers of two waves per SIMD (measured 4%
+// faster on 8192^3 than reading each step's operands before its MFMAs).
 template <int BN, int BT, int BK, int WN, int WT, int STAGES, int OUT, bool VEC, bool OUTL, bool F8,
           bool PERSIST = false>
 __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
@@ -294,26 +297,32 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
       }
     }
   };
-  // FP8: fragments of one 64-deep step (the chunks of int8 k-steps 2q and
-  // 2q + 1, read straight into the 8-register operands), then its MFMAs
-  auto step8 = [&](const int8_t* L, int q) {
+  // FP8: the operands of one 64-deep step are the chunks of int8 k-steps 2q and
+  // 2q + 1, read straight into 8-register operands.  The A fragments have two
+  // slots; each B fragment is re-read for the next step as soon as the last MFMA
+  // of this step that uses it has issued.
+  v8i ga[F8 ? 2 : 1][F8 ? RN : 1], gb[F8 ? RT : 1];
+  auto frag8 = [&](const int8_t* L, int base, int q) {
+    return __builtin_shufflevector(*reinterpret_cast<const v4i*>(L + base + cofs[2 * q]),
+                                   *reinterpret_cast<const v4i*>(L + base + cofs[2 * q + 1]), 0, 1, 2, 3, 4, 5,
+                                   6, 7);
+  };
+  auto readA8 = [&](int slot, const int8_t* L, int q) {
     if constexpr (F8) {
-      v8i a8[RN], b8[RT];
+#pragma unroll
+      for (int i = 0; i < RN; ++i) ga[slot][i] = frag8(L, a_base + i * 32 * BK, q);
+    }
+  };
+  auto readB8 = [&](int j, const int8_t* L, int q) {
+    if constexpr (F8) gb[j] = frag8(L, b_base + j * 32 * BK, q);
+  };
+  // the MFMAs of one B fragment (column block j of the wave tile)
+  auto col8 = [&](int slot, int j) {
+    if constexpr (F8) {
 #pragma unroll
       for (int i = 0; i < RN; ++i)
-        a8[i] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(L + a_base + cofs[2 * q] + i * 32 * BK),
-                                        *reinterpret_cast<const v4i*>(L + a_base + cofs[2 * q + 1] + i * 32 * BK),
-                                        0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int j = 0; j < RT; ++j)
-        b8[j] = __builtin_shufflevector(*reinterpret_cast<const v4i*>(L + b_base + cofs[2 * q] + j * 32 * BK),
-                                        *reinterpret_cast<const v4i*>(L + b_base + cofs[2 * q + 1] + j * 32 * BK),
-                                        0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int i = 0; i < RN; ++i)
-#pragma unroll
-        for (int j = 0; j < RT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8[i], b8[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[slot][i], gb[j], acc[i][j], 0, 0, 0, 127, 0,
+                                                                    127);
     }
   };
   // wait until at most `later` stages of this wave's DMA loads are in flight
@@ -354,17 +363,61 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
   bar();
 
   if constexpr (F8) {
-    for (int s = 0; s < nst; ++s) {
+    // As in the int8 schedule below, the last step of a stage runs half of its
+    // MFMAs, meets the other waves at the stage barrier, reads the next stage's
+    // first operands, then runs the other half.  The stage body has no branches
+    // (the last stages are separate copies): the MFMAs have no side effects, and
+    // across a branch the compiler would move them away from their reads.
+    constexpr int Q = KK / 2;
+    constexpr int H = RT / 2;   // B fragments whose MFMAs precede the stage barrier
+    static_assert(Q % 2 == 0 && RT % 2 == 0, "A slots alternate within a stage");
+    auto stage8 = [&](int s, auto more_c, auto issue_c) {
+      constexpr bool MORE = decltype(more_c)::value;   // a next stage follows
+      constexpr bool ISSUE = decltype(issue_c)::value; // stage s + STAGES exists
       const int8_t* L = lds + (s % STAGES) * STAGE_BYTES;
+      const int8_t* Ln = lds + ((s + 1) % STAGES) * STAGE_BYTES;
 #pragma unroll
-      for (int q = 0; q < KK / 2; ++q) step8(L, q);
-      if (s + 1 < nst) {
-        const int later = nst - 2 - s < STAGES - 2 ? nst - 2 - s : STAGES - 2;
-        wait_vm_lds(later);
-        bar();
-        if (s + STAGES < nst) issue(s % STAGES, (s + STAGES) * BK);
+      for (int q = 0; q < Q; ++q) {
+        const int cur = q & 1, nxt = cur ^ 1;
+        if (q + 1 < Q) {
+#pragma unroll
+          for (int j = 0; j < RT; ++j) {
+            col8(cur, j);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j == 0) readA8(nxt, L, q + 1);
+            readB8(j, L, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < H; ++j) col8(cur, j);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (MORE) {
+            wait_vm_lds(ISSUE ? STAGES - 2 : nst - 2 - s);
+            bar();
+            if constexpr (ISSUE) issue(s % STAGES, (s + STAGES) * BK);
+            readA8(nxt, Ln, 0);
+#pragma unroll
+            for (int j = 0; j < H; ++j) readB8(j, Ln, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = H; j < RT; ++j) {
+            col8(cur, j);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MORE) readB8(j, Ln, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
-    }
+    };
+    readA8(0, lds, 0);
+#pragma unroll
+    for (int j = 0; j < RT; ++j) readB8(j, lds, 0);
+    int s = 0;
+    for (; s + STAGES < nst; ++s) stage8(s, std::true_type{}, std::true_type{});
+    for (; s + 1 < nst; ++s) stage8(s, std::true_type{}, std::false_type{});
+    stage8(s, std::false_type{}, std::false_type{});
   } else {
   read_frags(0, lds, 0);
 
