@@ -419,41 +419,55 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     for (; s + 1 < nst; ++s) stage8(s, std::true_type{}, std::false_type{});
     stage8(s, std::false_type{}, std::false_type{});
   } else {
-  read_frags(0, lds, 0);
-
-  for (int s = 0; s < nst; ++s) {
-    const int8_t* L = lds + (s % STAGES) * STAGE_BYTES;
+    // Per stage: KK k-steps; each step's MFMAs run while the next step's
+    // fragments are read.  The last step runs PRE of its MFMAs, meets the other
+    // waves at the stage barrier (stage s + 1 must have landed, later ones may
+    // stay in flight; this wave's fragment reads of stage s must be complete),
+    // issues stage s + STAGES into the freed slot and reads stage s + 1's first
+    // fragments, then runs the rest.  With one or two waves per SIMD (the 128x128
+    // and 64x64 tiles) half of the MFMAs after the barrier cover those reads
+    // (512x4096x4096 2-4% faster); with four (16 waves of 256x256) the other
+    // waves cover them, and all before the barrier measured ~1% faster on 8192^3.
+    // As for FP8, the stage body has no branches, so the compiler keeps the
+    // MFMAs where they are written.
+    constexpr int PRE = NW >= 16 ? RN * RT : RN * RT / 2;
+    auto stage = [&](int s, auto more_c, auto issue_c) {
+      constexpr bool MORE = decltype(more_c)::value;   // a next stage follows
+      constexpr bool ISSUE = decltype(issue_c)::value; // stage s + STAGES exists
+      const int8_t* L = lds + (s % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < KK) {
-        read_frags(nxt, L, kk + 1);
-        mfmas(cur, 0, RN * RT);
-        // interleave the next step's 8 fragment reads with this step's MFMAs
+      for (int kk = 0; kk < KK; ++kk) {
+        const int cur = kk & 1, nxt = cur ^ 1;
+        if (kk + 1 < KK) {
+          read_frags(nxt, L, kk + 1);
+          mfmas(cur, 0, RN * RT);
+          // interleave the next step's fragment reads with this step's MFMAs
 #pragma unroll
-        for (int q = 0; q < RN + RT; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, (RN * RT) / (RN + RT), 0);   // MFMAs
+          for (int q = 0; q < RN + RT; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, (RN * RT) / (RN + RT), 0);   // MFMAs
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          mfmas(cur, 0, PRE);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (MORE) {
+            wait_vm_lds(ISSUE ? STAGES - 2 : nst - 2 - s);
+            bar();
+            if constexpr (ISSUE) issue(s % STAGES, (s + STAGES) * BK);
+            read_frags(nxt, lds + ((s + 1) % STAGES) * STAGE_BYTES, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas(cur, PRE, RN * RT - PRE);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        mfmas(cur, 0, RN * RT / 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < nst) {
-          // stage s+1 must have landed (later ones may stay in flight); this
-          // wave's fragment reads of stage s must be complete before the barrier
-          const int later = nst - 2 - s < STAGES - 2 ? nst - 2 - s : STAGES - 2;
-          wait_vm_lds(later);
-          bar();
-          if (s + STAGES < nst) issue(s % STAGES, (s + STAGES) * BK);
-          read_frags(nxt, lds + ((s + 1) % STAGES) * STAGE_BYTES, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(cur, RN * RT / 2, RN * RT - RN * RT / 2);
-        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-  }
+    };
+    read_frags(0, lds, 0);
+    int s = 0;
+    for (; s + STAGES < nst; ++s) stage(s, std::true_type{}, std::true_type{});
+    for (; s + 1 < nst; ++s) stage(s, std::true_type{}, std::false_type{});
+    stage(s, std::false_type{}, std::false_type{});
   }
 
   int next_tile = total_tiles;
