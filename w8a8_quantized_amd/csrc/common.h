@@ -89,7 +89,7 @@ __host__ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
-// Low bytes of four words -> one word (byte i from word i).// Low bytes of four words -> one word (byte i from word i).
+// Low bytes of four words -> one word (byte i from word i).
 __device__ __forceinline__ uint32_t pack4_lowbytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
   const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);

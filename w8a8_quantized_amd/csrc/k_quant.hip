@@ -33,7 +33,9 @@
 // binary32 quotient goes through the hardware conversion (see e4m3_pack4).
 //
 // The multiply mode (MODE 1) also serves the mixed-precision decomposition's
-// bulk rows, weights and activations alike, with s a 0/1 column mask.
+// bulk rows, weights and activations alike, with s a 0/1 column mask.  Weight
+// codes (NTS) are written with non-temporal stores, activation codes with
+// ordinary ones.
 //
 // Slow path (any shape/alignment): one workgroup per row, two passes over the
 // row with plain IEEE binary32 divisions; identical results.
@@ -41,6 +43,8 @@
 #include "kernels.h"
 
 namespace sq {
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // 8 consecutive elements of one row as raw bits.
 template <typename T> struct Raw8;
@@ -86,8 +90,8 @@ __device__ __forceinline__ void static_scale(const float* clip, float& scale, do
 // MODE: 0 = activations, per-row range (divide by s); 1 = weights, per-row range
 // (multiply by s); 2 = activations, given range *clip (divide by s).
 // FULL: K == CPT * 2048, every thread's chunks exist (no per-chunk masks).
-// F8: E4M3 codes (MODE 0 or 1) instead of int8.
-template <typename T, int MODE, bool HAS_S, int CPT, bool FULL, bool F8>
+// F8: E4M3 codes (MODE 0 or 1) instead of int8.  NTS: non-temporal code stores.
+template <typename T, int MODE, bool HAS_S, int CPT, bool FULL, bool F8, bool NTS>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A, int64_t R,
                                                          int64_t K, const float* __restrict__ s,
                                                          const float* __restrict__ clip,
@@ -165,7 +169,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
           o.y = pack4_lowbytes(quant_code_bits(v[j][4], rsc), quant_code_bits(v[j][5], rsc),
                                quant_code_bits(v[j][6], rsc), quant_code_bits(v[j][7], rsc));
         }
-        *reinterpret_cast<uint2*>(Q + r * K + c * 8) = o;
+        if constexpr (NTS) {
+          // weight codes are read back much later: non-temporal stores
+          // (8192 x 8192 fp32 weights 5% faster; activation codes, read by the
+          // GEMM right after, were slower this way)
+          u32x2 ov;
+          ov[0] = o.x;
+          ov[1] = o.y;
+          __builtin_nontemporal_store(ov, reinterpret_cast<u32x2*>(Q + r * K + c * 8));
+        } else {
+          *reinterpret_cast<uint2*>(Q + r * K + c * 8) = o;
+        }
       }
     }
   };
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(256) void quant_rows_slow_kernel(const T* __restric
   }
 }
 
-template <typename T, int MODE, bool HAS_S, bool F8>
+template <typename T, int MODE, bool HAS_S, bool F8, bool NTS>
 static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, const float* clip,
                              int8_t* Q, float* scale, int ncu, hipStream_t st) {
   const int64_t nchunks = K / 8;
@@ -255,8 +269,8 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, c
   const int c2 = cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8;   // instantiated sizes
   const bool full = K == (int64_t)c2 * 2048;
 #define SQ_QUANT_LAUNCH(C)                                                                              \
-  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true, F8>), grid, block, 0, st, A, R, K, s, clip, Q, scale); \
-  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false, F8>), grid, block, 0, st, A, R, K, s, clip, Q, scale);
+  if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true, F8, NTS>), grid, block, 0, st, A, R, K, s, clip, Q, scale); \
+  else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false, F8, NTS>), grid, block, 0, st, A, R, K, s, clip, Q, scale);
   switch (c2) {
     case 1: SQ_QUANT_LAUNCH(1) break;
     case 2: SQ_QUANT_LAUNCH(2) break;
@@ -267,12 +281,12 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, c
   return hipGetLastError();
 }
 
-template <typename T, int MODE, bool F8 = false>
+template <typename T, int MODE, bool F8 = false, bool NTS = false>
 static hipError_t quant_dispatch(const T* A, int64_t R, int64_t K, const float* s, const float* clip,
                                  int8_t* Q, float* scale, bool vec_ok, int ncu, hipStream_t st) {
   if (vec_ok && K <= kQuantFastMaxK) {
-    return s ? quant_fast<T, MODE, true, F8>(A, R, K, s, clip, Q, scale, ncu, st)
-             : quant_fast<T, MODE, false, F8>(A, R, K, s, clip, Q, scale, ncu, st);
+    return s ? quant_fast<T, MODE, true, F8, NTS>(A, R, K, s, clip, Q, scale, ncu, st)
+             : quant_fast<T, MODE, false, F8, NTS>(A, R, K, s, clip, Q, scale, ncu, st);
   }
   int64_t g = R < 8LL * ncu ? R : 8LL * ncu;
   hipLaunchKernelGGL((quant_rows_slow_kernel<T, MODE, F8>), dim3((unsigned)g), dim3(256), 0, st, A, R, K,
@@ -285,10 +299,11 @@ static hipError_t quant_mode(const T* A, int mode, int64_t R, int64_t K, const f
                              const float* clip, int8_t* Q, float* scale, bool vec_ok, int ncu,
                              hipStream_t st) {
   switch (mode) {
-    case kQuantWeights: return quant_dispatch<T, 1>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    case kQuantWeights: return quant_dispatch<T, 1, false, true>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    case kQuantActMasked: return quant_dispatch<T, 1>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
     case kQuantActStatic: return quant_dispatch<T, 2>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
     case kQuantActF8: return quant_dispatch<T, 0, true>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
-    case kQuantWeightsF8: return quant_dispatch<T, 1, true>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
+    case kQuantWeightsF8: return quant_dispatch<T, 1, true, true>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
     default: return quant_dispatch<T, 0>(A, R, K, s, clip, Q, scale, vec_ok, ncu, st);
   }
 }

@@ -24,10 +24,13 @@ hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, flo
                                 hipStream_t st);
 // Row quantiser modes: per-token activations (divide by s, per-row range),
 // per-output-channel weights (multiply by s, per-row range; also the
-// decomposition's bulk rows, with s a 0/1 column mask), activations against the
-// range *clip (divide by s, one scale for every row); and the first two with FP8
-// E4M3 codes (scale = row amax / 448).
-enum QuantMode { kQuantAct = 0, kQuantWeights = 1, kQuantActStatic = 2, kQuantActF8 = 3, kQuantWeightsF8 = 4 };
+// decomposition's bulk weight rows, with s a 0/1 column mask), activations against
+// the range *clip (divide by s, one scale for every row); the first two with FP8
+// E4M3 codes (scale = row amax / 448); and the decomposition's bulk activation
+// rows (multiply by the 0/1 mask, per-row range).  Weight codes are written with
+// non-temporal stores.
+enum QuantMode { kQuantAct = 0, kQuantWeights = 1, kQuantActStatic = 2, kQuantActF8 = 3, kQuantWeightsF8 = 4,
+                 kQuantActMasked = 5 };
 hipError_t launch_quant_rows(const void* A, bool bf16, int mode, int64_t R, int64_t K,
                              const float* s, const float* clip, int8_t* Q, float* scale,
                              bool vec_ok, int ncu, hipStream_t st);

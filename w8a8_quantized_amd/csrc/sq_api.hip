@@ -242,7 +242,7 @@ sq_status sq_decomp_quant_act(const void* X, sq_dtype x_t, int64_t T, int64_t K,
   if (n_o < 0 || n_o > K) return SQ_ERR_SHAPE;
   const bool vec = (K % 8 == 0) && rows_vec16(X, K, esize(x_t)) && aligned16(Xq);
   // per-row range and codes of X with the outlier columns multiplied by 0
-  if (sq::launch_quant_rows(X, x_t == SQ_BF16, sq::kQuantWeights, T, K, mask, nullptr, Xq, x_scale, vec,
+  if (sq::launch_quant_rows(X, x_t == SQ_BF16, sq::kQuantActMasked, T, K, mask, nullptr, Xq, x_scale, vec,
                             cu_count(), stream) != hipSuccess)
     return SQ_ERR_HIP;
   return hip_status(sq::launch_decomp_gather(X, x_t == SQ_BF16, T, K, idx, n_o, X_out, cu_count(), stream));
