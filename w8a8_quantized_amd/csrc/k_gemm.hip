@@ -418,6 +418,12 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     for (; s + STAGES < nst; ++s) stage8(s, std::true_type{}, std::true_type{});
     for (; s + 1 < nst; ++s) stage8(s, std::true_type{}, std::false_type{});
     stage8(s, std::false_type{}, std::false_type{});
+    // keep the last stage's MFMAs here: sunk into the epilogue, next to its
+    // cached channel scales, they made the compiler spill
+#pragma unroll
+    for (int i = 0; i < RN; ++i)
+#pragma unroll
+      for (int j = 0; j < RT; ++j) asm volatile("" : "+v"(acc[i][j]));
   } else {
     // Per stage: KK k-steps; each step's MFMAs run while the next step's
     // fragments are read.  The last step runs PRE of its MFMAs, meets the other
