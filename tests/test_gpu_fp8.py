@@ -106,6 +106,24 @@ def test_fp8_gemm_accuracy(sq, T, N, K):
     print(f"fp8 gemm {T}x{N}x{K}: max |acc - exact| / sum|p| = {r:.3g}")
 
 
+# One, two and three 128-byte K stages (with K tails) on both FP8 tiles: 128x128
+# (fewer than 256 tiles of 256x256) and 256x256 with 8 waves; outputs sampled on
+# the larger shape, edges included.
+@pytest.mark.parametrize("T,N,K", [(300, 520, 112), (300, 520, 208), (300, 520, 336),
+                                   (2100, 8200, 64), (2100, 8200, 208), (2100, 8200, 336)])
+def test_fp8_gemm_stage_counts(sq, T, N, K):
+    X, W, s = _case(5 * T + N + K, T, K, N, "f32")
+    Xq_r, xs_r = O.quant_act_fp8(X, s)
+    Wq_r, ws_r = O.quantize_weights_fp8(W, s)
+    ti = ni = None
+    if T * N > 1_000_000:
+        rng = np.random.default_rng(T + K)
+        m = 200_000
+        ti = np.concatenate([rng.integers(0, T, m), np.full(N, T - 1), np.arange(T)])
+        ni = np.concatenate([rng.integers(0, N, m), np.arange(N), np.full(T, N - 1)])
+    _check_gemm(sq, Xq_r, xs_r, Wq_r, ws_r, ti, ni)
+
+
 def test_fp8_gemm_misaligned_generic(sq):
     X, W, s = _case(9, 20, 64, 36, "f32")
     Xq_r, xs_r = O.quant_act_fp8(X, s)

@@ -165,12 +165,16 @@ def _codes(rng, r, k):
 GEMM_SHAPES = [
     # decode kernel (T <= 64)
     (1, 1, 16), (1, 40, 64), (5, 129, 80), (16, 1000, 256), (17, 77, 1040), (33, 64, 48), (64, 300, 528),
-    # prefill kernel, 64x64 tiles (< 256 tiles of 128x128), ragged edges and K tails
-    (65, 40, 16), (100, 129, 64), (300, 1000, 80), (257, 513, 1040), (512, 1024, 4096),
-    # prefill kernel, 128x128 tiles (>= 256 of them, < 256 of 256x256), ragged edges and K tails
-    (1000, 4100, 272), (1100, 4000, 1040),
-    # prefill kernel, 256x256 tiles (>= 256 tiles), ragged edges and a K tail
-    (2100, 8200, 48), (2048, 8192, 64),
+    # prefill kernel, 64x64 tiles (< 256 tiles of 128x128; 256-byte K stages), ragged
+    # edges and K tails; one, two, three and more stages
+    (65, 40, 16), (100, 129, 64), (300, 1000, 80), (100, 129, 304), (65, 40, 688), (257, 513, 1040),
+    (512, 1024, 4096),
+    # prefill kernel, 128x128 tiles (>= 256 of them, < 256 of 256x256; 256-byte K
+    # stages), ragged edges and K tails; one, two, three and five stages
+    (1000, 4100, 208), (1000, 4100, 272), (1000, 4100, 608), (1100, 4000, 1040),
+    # prefill kernel, 256x256 tiles (more than 256 of them: the persistent form;
+    # 128-byte K stages), ragged edges and K tails; one, two and three stages
+    (2100, 8200, 48), (2048, 8192, 64), (2100, 8200, 208), (2048, 8448, 256), (2100, 8200, 336),
     # generic kernel (K % 16 != 0)
     (3, 5, 7), (70, 33, 83), (1, 1, 1),
 ]
@@ -187,7 +191,8 @@ def test_gemm_int32_accumulators(sq, T, N, K):
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("T,N,K", [(1, 40, 64), (17, 77, 1040), (300, 1000, 80), (2100, 8200, 48),
-                                   (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272)])
+                                   (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272),
+                                   (100, 129, 688), (1000, 4100, 608), (2100, 8200, 336)])
 def test_gemm_epilogue(sq, out, T, N, K):
     rng = np.random.default_rng(T + N + K)
     Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)
