@@ -750,8 +750,8 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st, int ncu = 0) {
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   if (a.f8) {
-    // 8 waves of 64 x 128: the FP8 step needs ~170 registers per wave, more
-    // than the 16-wave tile allows
+    // 8 waves of 64 x 128: the FP8 step's 8-register operands and their
+    // second slot need ~240 registers per wave, more than the 16-wave tile allows
     const int64_t big8 = ((a.N + 255) / 256) * ((a.T + 255) / 256);
     if (big8 >= ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true>(a, st);
     return gemm_cfg<128, 128, 128, 2, 2, 2, true>(a, st);
