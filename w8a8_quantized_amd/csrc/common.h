@@ -24,6 +24,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (f != f) ? 0x7FC0u : r;
 }
 
+// Two binary32 values -> a bfloat16 pair (a in the low half) by one hardware
+// conversion (v_cvt_pk_bf16_f32, nearest with ties to even).  For every non-NaN
+// binary32 input it gives the bits of f32_to_bf16 (checked on the GPU over all
+// 2^32 patterns, subnormals and overflow to infinity included); a NaN stays a NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Correctly rounded binary32 quotient a / b from a binary64 reciprocal:
 //   RN32(a / b) == (float)((double)a * rb)   with rb = RN64(1 / (double)b).
 // Why: a/b is never a binary32 rounding midpoint, and for 24-bit a and b it

@@ -61,8 +61,8 @@ __device__ __forceinline__ void store4(void* Y, int64_t off, int nrem, const A* 
     uint16_t* y = static_cast<uint16_t*>(Y) + off;
     if (VEC) {
       uint2 p;
-      p.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      p.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      p.x = f32x2_to_bf16x2(v[0], v[1]);
+      p.y = f32x2_to_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(y) = p;
       return;
     }
@@ -599,8 +599,8 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
                 *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
               } else {
                 uint2 p;
-                p.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-                p.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+                p.x = f32x2_to_bf16x2(v[0], v[1]);
+                p.y = f32x2_to_bf16x2(v[2], v[3]);
                 *reinterpret_cast<uint2*>(dst) = p;
               }
             }

@@ -382,8 +382,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
         uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)t * ldy + n;
         if (vec) {
           uint2 pk;
-          pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-          pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+          pk.x = f32x2_to_bf16x2(v[0], v[1]);
+          pk.y = f32x2_to_bf16x2(v[2], v[3]);
           *reinterpret_cast<uint2*>(y) = pk;
         } else {
           for (int e = 0; e < 4 && e < nrem; ++e) y[e] = (uint16_t)f32_to_bf16(v[e]);
