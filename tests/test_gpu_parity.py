@@ -205,6 +205,37 @@ def test_gemm_epilogue(sq, out, T, N, K):
     assert_out_close(host(y), y_r, out)
 
 
+def _bf16_edge_values():
+    """binary32 values at the hard cases of rounding to bf16: exact ties with an
+    even and an odd kept half, one ulp either side of a tie, subnormals, and the
+    top of the range (the tie between the largest finite bf16 and infinity)."""
+    lows = [0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF]
+    exps = [1, 2, 20, 100, 126, 127, 128, 150, 200, 253, 254]
+    bits = [(e << 23) | (h << 16) | lo for e in exps for h in (0x00, 0x01, 0x7E, 0x7F) for lo in lows]
+    bits += [(h << 16) | lo for h in (0x00, 0x01, 0x40, 0x7F) for lo in lows[1:]]   # subnormals
+    bits = np.array(bits, np.uint32)
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("T,N,K", [(16, 64, 64), (300, 1000, 64), (2100, 8200, 48)])
+def test_gemm_bf16_rounding_edges(sq, T, N, K):
+    """One-hot codes make every accumulator 1, so y = fl32(x_scale * w_scale); the
+    scales put rounding ties, subnormals and overflow into the bf16 epilogue
+    (decode kernel, 64x64 tiles, persistent 256x256 tiles)."""
+    v = _bf16_edge_values()
+    xs = np.resize(v, T).astype(np.float32)
+    ws = np.resize(np.array([1.0, -1.0, 1.0 + 2.0 ** -9, 3.0, 2.0 ** -20, 0.7], np.float32), N)
+    Xq = np.zeros((T, K), np.int8)
+    Wq = np.zeros((N, K), np.int8)
+    Xq[:, 0] = 1
+    Wq[:, 0] = 1
+    y = sq.sq_w8a8_gemm(torch.from_numpy(Xq).to(DEV), torch.from_numpy(xs).to(DEV),
+                        torch.from_numpy(Wq).to(DEV), torch.from_numpy(ws).to(DEV), out_dtype=torch.bfloat16)
+    y_r = O.dequant(np.ones((T, N), np.int32), xs, ws)
+    assert np.array_equal(host(y), O.to_bf16(y_r))
+
+
 def test_gemm_unaligned_output_row(sq):
     """N % 4 != 0: element stores on the edge, same values."""
     rng = np.random.default_rng(5)
