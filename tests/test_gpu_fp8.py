@@ -106,10 +106,11 @@ def test_fp8_gemm_accuracy(sq, T, N, K):
     print(f"fp8 gemm {T}x{N}x{K}: max |acc - exact| / sum|p| = {r:.3g}")
 
 
-# One, two and three 128-byte K stages (with K tails) on both FP8 tiles: 128x128
-# (fewer than 256 tiles of 256x256) and 256x256 with 8 waves; outputs sampled on
-# the larger shape, edges included.
-@pytest.mark.parametrize("T,N,K", [(300, 520, 112), (300, 520, 208), (300, 520, 336),
+# One, two and three K stages (with K tails) on every FP8 tile: 64x64 and 128x128
+# (256-byte stages) and the persistent 256x256 with 8 waves (128-byte stages);
+# outputs sampled on the larger shapes, edges included.
+@pytest.mark.parametrize("T,N,K", [(300, 520, 112), (300, 520, 336), (300, 520, 608),
+                                   (1000, 4100, 208), (1000, 4100, 336), (1000, 4100, 608),
                                    (2100, 8200, 64), (2100, 8200, 208), (2100, 8200, 336)])
 def test_fp8_gemm_stage_counts(sq, T, N, K):
     X, W, s = _case(5 * T + N + K, T, K, N, "f32")

@@ -370,7 +370,7 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     // across a branch the compiler would move them away from their reads.
     constexpr int Q = KK / 2;
     constexpr int H = RT / 2;   // B fragments whose MFMAs precede the stage barrier
-    static_assert(Q % 2 == 0 && RT % 2 == 0, "A slots alternate within a stage");
+    static_assert(Q % 2 == 0, "A slots alternate within a stage");
     auto stage8 = [&](int s, auto more_c, auto issue_c) {
       constexpr bool MORE = decltype(more_c)::value;   // a next stage follows
       constexpr bool ISSUE = decltype(issue_c)::value; // stage s + STAGES exists
@@ -762,7 +762,11 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
     // once per tile, outside the K loop).
     const int64_t big8 = ((a.N + 255) / 256) * ((a.T + 255) / 256);
     if (big8 >= ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true, true>(a, st, ncu);
-    return gemm_cfg<128, 128, 128, 2, 2, 2, true>(a, st);
+    // smaller problems: the int8 choice of tiles (128x128, else 64x64) with two
+    // 256-byte K stages
+    const int64_t mid8 = ((a.N + 127) / 128) * ((a.T + 127) / 128);
+    if (mid8 >= ncu) return gemm_cfg<128, 128, 256, 2, 2, 2, true>(a, st);
+    return gemm_cfg<64, 64, 256, 2, 2, 2, true>(a, st);
   }
   // 256x256 tiles when they fill the chip at least once; the big tile runs 16
   // waves of 64x64 (4 per SIMD): with fewer, larger wave tiles the per-stage
