@@ -164,8 +164,10 @@ constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 1
 // from global memory per quadruple.
 //
 // F8 (FP8 E4M3 operands, inferenceinterviews.com formats paragraph): the same
-// byte tiles feed v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) with
-// binary32 accumulators.  One MFMA takes, per lane, the two 16-byte chunks that
+// byte tiles feed v_mfma_f32_32x32x64_f8f6f4 with binary32 accumulators (the
+// compiler selects the unscaled instruction for the scaled builtin with zero
+// scale operands; on the GPU it gives the bits of the scaled form with E8M0 unit
+// scales, 127, on 4M random outputs, and issues without the scale operands).  One MFMA takes, per lane, the two 16-byte chunks that
 // two consecutive int8 k-steps would take, for A and B alike, so every product
 // pairs the same k.  FP8 runs 8 waves of 64x128 per 256x256 tile (the operands
 // are twice as wide per lane, and the 16-wave layout would spill); the A
@@ -321,8 +323,7 @@ __global__ __launch_bounds__(WN* WT * 64) void gemm_i8_mfma_kernel(
     if constexpr (F8) {
 #pragma unroll
       for (int i = 0; i < RN; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[slot][i], gb[j], acc[i][j], 0, 0, 0, 127, 0,
-                                                                    127);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[slot][i], gb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
     }
   };
   // wait until at most `later` stages of this wave's DMA loads are in flight

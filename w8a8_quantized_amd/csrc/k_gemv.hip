@@ -106,7 +106,9 @@ __device__ __forceinline__ void gemv_outlier_sums(float (&so)[NB][TB][4], int n_
 // Requires K % 16 == 0, N * K < 2^31 and T * K < 2^31 (the host splits larger N),
 // 16-byte aligned Xq and Wq.  KW waves per workgroup, which owns NB*16 channels.
 // F8: the codes are FP8 E4M3 and each pair of 64-byte k-steps is one
-// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales, binary32 accumulators):
+// v_mfma_f32_16x16x128_f8f6f4 (binary32 accumulators; the scaled builtin with
+// zero scale operands, for which the compiler selects the unscaled instruction,
+// bit-identical on the GPU to E8M0 unit scales):
 // a lane joins the two 16-byte chunks it would take for the two int8 steps, for
 // the weights and the token codes alike, so every product pairs the same k.
 // OUTL: the epilogue adds the binary32 outlier-channel product of the
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
             const v8i x8 = __builtin_shufflevector(xv[sl][b][m], xv[sl][b][m + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, x8, acc[i][b], 0, 0, 0, 127, 0, 127);
+            acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, x8, acc[i][b], 0, 0, 0, 0, 0, 0);
           }
         }
       }
