@@ -759,8 +759,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
     // 8 waves of 64 x 128: the FP8 step's 8-register operands and their
     // second slot need ~240 registers per wave, more than the 16-wave tile allows.
     // More tiles than CUs: the persistent form, as for int8 (1.2% faster on
-    // 8192^3 and 2048x16384x4096; the tile loop's few extra values are spilled
-    // once per tile, outside the K loop).
+    // 8192^3 and 2048x16384x4096).
     const int64_t big8 = ((a.N + 255) / 256) * ((a.T + 255) / 256);
     if (big8 >= ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true, true>(a, st, ncu);
     // smaller problems: the int8 choice of tiles (128x128, else 64x64) with two
