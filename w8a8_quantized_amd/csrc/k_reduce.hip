@@ -31,14 +31,27 @@ __global__ void fill2_f32_kernel(float* __restrict__ p, float* __restrict__ q, i
 
 // Element loaders: VEC elements of one row starting at column c.
 template <typename T, int VEC> struct ChunkLoad;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes, with a non-temporal hint when NT (data read once: it then does not
+// displace what a following kernel reads again from the Infinity Cache).
+template <bool NT> __device__ __forceinline__ f32x4_t load16f(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  else return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <bool NT> __device__ __forceinline__ u32x4_t load16u(const uint16_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else return *reinterpret_cast<const u32x4_t*>(p);
+}
+
 template <> struct ChunkLoad<float, 4> {
-  static __device__ __forceinline__ void abs(const float* p, float* o) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    o[0] = fabsf(v.x); o[1] = fabsf(v.y); o[2] = fabsf(v.z); o[3] = fabsf(v.w);
+  template <bool NT = false> static __device__ __forceinline__ void abs(const float* p, float* o) {
+    const f32x4_t v = load16f<NT>(p);
+    o[0] = fabsf(v[0]); o[1] = fabsf(v[1]); o[2] = fabsf(v[2]); o[3] = fabsf(v[3]);
   }
 };
 template <> struct ChunkLoad<uint16_t, 8> {
-  static __device__ __forceinline__ void abs(const uint16_t* p, float* o) {
+  template <bool NT = false> static __device__ __forceinline__ void abs(const uint16_t* p, float* o) {
     uint4 v = *reinterpret_cast<const uint4*>(p);
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -49,10 +62,12 @@ template <> struct ChunkLoad<uint16_t, 8> {
   }
 };
 template <> struct ChunkLoad<float, 1> {
-  static __device__ __forceinline__ void abs(const float* p, float* o) { o[0] = fabsf(*p); }
+  template <bool NT = false> static __device__ __forceinline__ void abs(const float* p, float* o) { o[0] = fabsf(*p); }
 };
 template <> struct ChunkLoad<uint16_t, 1> {
-  static __device__ __forceinline__ void abs(const uint16_t* p, float* o) { o[0] = fabsf(bf16_to_f32(*p)); }
+  template <bool NT = false> static __device__ __forceinline__ void abs(const uint16_t* p, float* o) {
+    o[0] = fabsf(bf16_to_f32(*p));
+  }
 };
 
 // Running maximum of |x| over a chunk of VEC columns.  bf16 chunks keep four
@@ -67,9 +82,9 @@ template <typename T, int VEC> struct ColMax {
 #pragma unroll
     for (int i = 0; i < VEC; ++i) m[i] = 0.0f;
   }
-  __device__ __forceinline__ void add(const T* p) {
+  template <bool NT = false> __device__ __forceinline__ void add(const T* p) {
     float a[VEC];
-    ChunkLoad<T, VEC>::abs(p, a);
+    ChunkLoad<T, VEC>::template abs<NT>(p, a);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) m[i] = fmaxf(m[i], a[i]);
   }
@@ -81,9 +96,9 @@ template <typename T, int VEC> struct ColMax {
 template <> struct ColMax<uint16_t, 8> {
   uint32_t pm[4];
   __device__ __forceinline__ void init() { pm[0] = pm[1] = pm[2] = pm[3] = 0u; }
-  __device__ __forceinline__ void add(const uint16_t* p) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+  template <bool NT = false> __device__ __forceinline__ void add(const uint16_t* p) {
+    const u32x4_t v = load16u<NT>(p);
+    const uint32_t w[4] = {v[0] & 0x7FFF7FFFu, v[1] & 0x7FFF7FFFu, v[2] & 0x7FFF7FFFu, v[3] & 0x7FFF7FFFu};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       pm[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, pm[q]),
@@ -145,7 +160,7 @@ __global__ __launch_bounds__(256) void col_absmax_kernel(const T* __restrict__ A
 // of short slabs; for bf16 alone the slab form stays ahead).  Rows past the end
 // repeat the workgroup's previous row (harmless for a maximum), so the loads
 // carry no conditions.  Requires S <= rows and 16-byte aligned rows.
-template <typename T, int U>
+template <typename T, int U, bool NT = false>
 __device__ __forceinline__ void colmax_block(const T* __restrict__ A, int64_t rows, int64_t cols, int64_t x,
                                              int64_t y, int64_t S, float* __restrict__ amax) {
   constexpr int VEC = 16 / sizeof(T);
@@ -159,7 +174,7 @@ __device__ __forceinline__ void colmax_block(const T* __restrict__ A, int64_t ro
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t rr = r + u * S;
-      acc.add(p + (rr < rows ? rr : last) * cols);
+      acc.template add<NT>(p + (rr < rows ? rr : last) * cols);
     }
     last = r;
   }
@@ -181,7 +196,11 @@ __global__ __launch_bounds__(256) void col_absmax_blk_kernel(const T* __restrict
 // of W.  SX and SW are chosen so that every workgroup reads about the same
 // bytes, about one workgroup per CU in all; the two streams then share the chip
 // instead of following each other (8192 x 8192 bf16 X and fp32 W: 66 us against
-// 78 us for the two launches).
+// 78 us for the two launches).  X is read with non-temporal loads: the calibration
+// activations are not read again, while W is quantised next, and with X out of
+// the Infinity Cache more of W is still there (pass and weight quantiser together
+// ~6 us faster on 8192 x 8192; W read that way too made the quantiser 16 us
+// slower).
 template <typename TX, typename TW, int U>
 __global__ __launch_bounds__(256) void col_absmax_pair_kernel(const TX* __restrict__ X, int64_t T, int64_t cbX,
                                                               int64_t SX, const TW* __restrict__ W, int64_t N,
@@ -189,7 +208,7 @@ __global__ __launch_bounds__(256) void col_absmax_pair_kernel(const TX* __restri
                                                               float* __restrict__ xa, float* __restrict__ wa) {
   const int64_t g = blockIdx.x, nX = cbX * SX;
   if (g < nX) {
-    colmax_block<TX, U>(X, T, K, g % cbX, g / cbX, SX, xa);
+    colmax_block<TX, U, true>(X, T, K, g % cbX, g / cbX, SX, xa);
   } else {
     const int64_t h = g - nX;
     colmax_block<TW, U>(W, N, K, h % cbW, h / cbW, SW, wa);
