@@ -116,3 +116,25 @@ def test_decomp_gemm_graph_replays(sq):
         want = sq.sq_decomp_gemm(Xq_e, xs_e, Wq, ws, Xo_e, Wo, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert np.array_equal(host(Y_g), host(want)), f"replay {r}"
+
+
+@pytest.mark.parametrize("T,N,K", [(2100, 8200, 208), (300, 520, 336), (16, 640, 512)])
+def test_fp8_gemm_graph_replays(sq, T, N, K):
+    """sq_fp8_gemm (persistent 256x256 form, 64x64 tiles, decode kernel) with its
+    FP8 operands copied into the captured buffers before each replay."""
+    rng = np.random.default_rng(T + N + K)
+    W = torch.from_numpy((rng.standard_normal((N, K)) * 0.05).astype(np.float32)).to(DEV)
+    Wq, ws = sq.sq_quantize_weights_fp8(W)
+    X_in = _draw(rng, T, K)
+    Xq_in, xs_in = sq.sq_quant_act_fp8(X_in)
+    Y_g = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    g = _capture(lambda: sq.sq_fp8_gemm(Xq_in, xs_in, Wq, ws, Y=Y_g))
+    for r in range(4):
+        Xq, xs = sq.sq_quant_act_fp8(_draw(rng, T, K, scale=1.0 + r))
+        Xq_in.copy_(Xq)
+        xs_in.copy_(xs)
+        g.replay()
+        torch.cuda.synchronize()
+        want = sq.sq_fp8_gemm(Xq, xs, Wq, ws)   # eager, own output
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y_g), host(want)), f"replay {r}"
