@@ -140,7 +140,7 @@ def test_fp8_gemm_misaligned_generic(sq):
 
 
 @pytest.mark.parametrize("name", ["heavy_t8192_k8192_n8192", "prefill_t2048_k4096_n16384",
-                                  "decode_t16_k8192_n28672"])
+                                  "decode_t16_k8192_n28672", "page_t512_k4096_n4096", "tiny_t128_k1024_n1024"])
 def test_fp8_full_size(sq, name):
     """The workload's smoothed operands in FP8: all codes and scales; the GEMM on
     sampled (t, n) pairs against exact dot products."""
