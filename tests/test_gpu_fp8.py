@@ -107,10 +107,12 @@ def test_fp8_gemm_accuracy(sq, T, N, K):
 
 
 # One, two and three K stages (with K tails) on every FP8 tile: 64x64 and 128x128
-# (256-byte stages) and the persistent 256x256 with 8 waves (128-byte stages);
+# (256-byte stages), 64x128 (128-byte stages) and the persistent 256x256 with 8
+# waves (128-byte stages);
 # outputs sampled on the larger shapes, edges included.
 @pytest.mark.parametrize("T,N,K", [(300, 520, 112), (300, 520, 336), (300, 520, 608),
                                    (1000, 4100, 208), (1000, 4100, 336), (1000, 4100, 608),
+                                   (100, 12800, 112), (100, 12800, 208), (128, 16384, 336),
                                    (2100, 8200, 64), (2100, 8200, 208), (2100, 8200, 336)])
 def test_fp8_gemm_stage_counts(sq, T, N, K):
     X, W, s = _case(5 * T + N + K, T, K, N, "f32")

@@ -172,6 +172,10 @@ GEMM_SHAPES = [
     # prefill kernel, 128x128 tiles (>= 256 of them, < 256 of 256x256; 256-byte K
     # stages), ragged edges and K tails; one, two, three and five stages
     (1000, 4100, 208), (1000, 4100, 272), (1000, 4100, 608), (1100, 4000, 1040),
+    # prefill kernel, 64x128 tiles (65-128 tokens, at least 3/4 of the CUs' worth of
+    # 64-channel tiles; 128-byte K stages), ragged edges and K tails; one, two,
+    # three and six stages
+    (100, 12800, 48), (100, 12800, 208), (128, 16384, 336), (65, 14336, 656),
     # prefill kernel, 256x256 tiles (more than 256 of them: the persistent form;
     # 128-byte K stages), ragged edges and K tails; one, two and three stages
     (2100, 8200, 48), (2048, 8192, 64), (2100, 8200, 208), (2048, 8448, 256), (2100, 8200, 336),
@@ -192,7 +196,8 @@ def test_gemm_int32_accumulators(sq, T, N, K):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("T,N,K", [(1, 40, 64), (17, 77, 1040), (300, 1000, 80), (2100, 8200, 48),
                                    (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272),
-                                   (100, 129, 688), (1000, 4100, 608), (2100, 8200, 336)])
+                                   (100, 129, 688), (1000, 4100, 608), (2100, 8200, 336),
+                                   (100, 12800, 208), (65, 14336, 656)])
 def test_gemm_epilogue(sq, out, T, N, K):
     rng = np.random.default_rng(T + N + K)
     Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)
