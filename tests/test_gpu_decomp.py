@@ -65,7 +65,8 @@ def _check_split(Xq_g, xs_g, Xo_g, Xq_r, xs_r, Xo_r, idx):
 @pytest.mark.parametrize("xdt", ["f32", "bf16"])
 @pytest.mark.parametrize("T,N,K,n_o", [(1, 8, 16, 1), (16, 300, 512, 7), (70, 200, 1040, 4),
                                        (300, 520, 2048, 12), (33, 64, 133, 2), (129, 136, 256, 0),
-                                       (40, 72, 256, 9), (5, 96, 1024, 250), (100, 12800, 512, 9)])
+                                       (40, 72, 256, 9), (5, 96, 1024, 250), (100, 12800, 512, 9),
+                                       (200, 24576, 256, 9)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_decomp_layer(sq, xdt, T, N, K, n_o, out):
     rng = np.random.default_rng(T * 7 + N + K + n_o)

@@ -113,6 +113,7 @@ def test_fp8_gemm_accuracy(sq, T, N, K):
 @pytest.mark.parametrize("T,N,K", [(300, 520, 112), (300, 520, 336), (300, 520, 608),
                                    (1000, 4100, 208), (1000, 4100, 336), (1000, 4100, 608),
                                    (100, 12800, 112), (100, 12800, 208), (128, 16384, 336),
+                                   (768, 16384, 208), (200, 24576, 336), (100, 24600, 208),
                                    (2100, 8200, 64), (2100, 8200, 208), (2100, 8200, 336)])
 def test_fp8_gemm_stage_counts(sq, T, N, K):
     X, W, s = _case(5 * T + N + K, T, K, N, "f32")

@@ -176,6 +176,11 @@ GEMM_SHAPES = [
     # 64-channel tiles; 128-byte K stages), ragged edges and K tails; one, two,
     # three and six stages
     (100, 12800, 48), (100, 12800, 208), (128, 16384, 336), (65, 14336, 656),
+    # 65-128 tokens on 3/4 of the CUs' worth of 128-channel tiles: 128x128 tiles
+    (100, 24600, 208),
+    # prefill kernel, 256x256 tiles one per workgroup (3/4 to 1 per CU) and 128x256
+    # tiles (3/4 of the CUs or more), ragged edges and K tails
+    (768, 16384, 208), (1000, 12300, 80), (200, 24576, 336), (300, 24600, 48),
     # prefill kernel, 256x256 tiles (more than 256 of them: the persistent form;
     # 128-byte K stages), ragged edges and K tails; one, two and three stages
     (2100, 8200, 48), (2048, 8192, 64), (2100, 8200, 208), (2048, 8448, 256), (2100, 8200, 336),
@@ -197,7 +202,8 @@ def test_gemm_int32_accumulators(sq, T, N, K):
 @pytest.mark.parametrize("T,N,K", [(1, 40, 64), (17, 77, 1040), (300, 1000, 80), (2100, 8200, 48),
                                    (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272),
                                    (100, 129, 688), (1000, 4100, 608), (2100, 8200, 336),
-                                   (100, 12800, 208), (65, 14336, 656)])
+                                   (100, 12800, 208), (65, 14336, 656), (768, 16384, 208),
+                                   (200, 24576, 336)])
 def test_gemm_epilogue(sq, out, T, N, K):
     rng = np.random.default_rng(T + N + K)
     Xq, Wq = _codes(rng, T, K), _codes(rng, N, K)

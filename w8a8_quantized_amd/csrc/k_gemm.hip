@@ -763,7 +763,11 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
     const int64_t big8 = ((a.N + 255) / 256) * ((a.T + 255) / 256);
     if (big8 >= ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true, true>(a, st, ncu);
     // smaller problems: the int8 choice of tiles
+    if (4 * big8 >= 3 * ncu) return gemm_cfg<256, 256, 128, 4, 2, 2, true>(a, st);
+    if (a.T <= 128 && (a.N + 127) / 128 >= (3 * ncu) / 4) return gemm_cfg<128, 128, 256, 2, 2, 2, true>(a, st);
     if (a.T <= 128 && (a.N + 63) / 64 >= (3 * ncu) / 4) return gemm_cfg<64, 128, 128, 2, 2, 3, true>(a, st);
+    const int64_t tall8 = ((a.N + 127) / 128) * ((a.T + 255) / 256);
+    if (4 * tall8 >= 3 * ncu) return gemm_cfg<128, 256, 128, 2, 4, 2, true>(a, st);
     const int64_t mid8 = ((a.N + 127) / 128) * ((a.T + 127) / 128);
     if (mid8 >= ncu) return gemm_cfg<128, 128, 256, 2, 2, 2, true>(a, st);
     return gemm_cfg<64, 64, 256, 2, 2, 2, true>(a, st);
@@ -781,13 +785,27 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // epilogue; measured 2-3% faster on 8192^3 and 2048x16384x4096).
   const int64_t big = ((a.N + 255) / 256) * ((a.T + 255) / 256);
   if (big >= ncu) return gemm_cfg<256, 256, 128, 4, 4, 2, false, true>(a, st, ncu);
+  // At least 3/4 of a 256x256 tile per CU: the big tile still, one per workgroup;
+  // its operand reuse outweighs the idle CUs (768x16384x4096 64.0 against 82.9 us,
+  // 512x28672x8192 142 against 212 us with 128x128 tiles; at half the CUs it
+  // loses: 384x16384x8192 102.8 against 93.4 us).
+  if (4 * big >= 3 * ncu) return gemm_cfg<256, 256, 128, 4, 4, 2>(a, st);
   // Up to 128 tokens with many output channels (a batch of decode steps through
-  // a wide layer): one 128-token tile per 64 channels reads every weight tile
-  // once, where 64x64 tiles read it once per 64 tokens; three 128-byte stages.
-  // With weights streamed from HBM: 80x28672x8192 56.2 against 68.2 us,
-  // 128x14336x4096 20.7 against 24.4 us; with fewer channel tiles than 3/4 of
-  // the CUs 64x64 tiles stay ahead (8192 channels: 30.7 against 31.3 us).
+  // a wide layer): one 128-token tile per 128 channels (when those fill 3/4 of
+  // the CUs), else per 64 channels (three 128-byte stages), reads every weight
+  // tile once, where 64x64 tiles read it once per 64 tokens.  With weights
+  // streamed from HBM: 96x28672x8192 57.6 (128x128) / 61.2 (64x128) against 69
+  // us, 128x14336x4096 20.7 (64x128) against 24.4 us; with fewer channel tiles
+  // than 3/4 of the CUs 64x64 tiles stay ahead (8192 channels: 30.7 against 31.3 us).
+  if (a.T <= 128 && (a.N + 127) / 128 >= (3 * ncu) / 4) return gemm_cfg<128, 128, 256, 2, 2, 2>(a, st);
   if (a.T <= 128 && (a.N + 63) / 64 >= (3 * ncu) / 4) return gemm_cfg<64, 128, 128, 2, 2, 3>(a, st);
+  // Else 128 channels x 256 tokens (8 waves of 64x64, two 128-byte stages) when
+  // those tiles fill 3/4 of the CUs: fewer weight re-reads than 128x128 tiles
+  // (200x24576x4096 42.1 against 52.8 us, 512x14336x4096 43.0 against 52.5 us,
+  // 129-256 x 28672 x 8192 79-87 against 100-115 us; at half the CUs it loses:
+  // 160x16384x4096 39.2 against 28.8 us).
+  const int64_t tall = ((a.N + 127) / 128) * ((a.T + 255) / 256);
+  if (4 * tall >= 3 * ncu) return gemm_cfg<128, 256, 128, 2, 4, 2>(a, st);
   const int64_t mid = ((a.N + 127) / 128) * ((a.T + 127) / 128);
   if (mid >= ncu) return gemm_cfg<128, 128, 256, 2, 2, 2>(a, st);
   return gemm_cfg<64, 64, 256, 2, 2, 2>(a, st);
