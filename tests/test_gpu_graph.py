@@ -46,7 +46,7 @@ def _draw(rng, T, K, scale=1.0):
 
 @pytest.mark.parametrize("T,N,K", [(300, 384, 512), (16, 512, 1024)])
 def test_linear_graph_replays(sq, T, N, K):
-    """sq_w8a8_linear (quantiser + GEMM, or the decode GEMM at T <= 64)."""
+    """sq_w8a8_linear (quantiser + GEMM, or the decode GEMM at T <= 32)."""
     rng = np.random.default_rng(T + N + K)
     w = WL.page_tiny_fixture(seed=11, T=T, N=N, K=K)
     W = torch.from_numpy(w.W).to(DEV)

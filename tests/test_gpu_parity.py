@@ -163,8 +163,9 @@ def _codes(rng, r, k):
 
 
 GEMM_SHAPES = [
-    # decode kernel (T <= 64)
-    (1, 1, 16), (1, 40, 64), (5, 129, 80), (16, 1000, 256), (17, 77, 1040), (33, 64, 48), (64, 300, 528),
+    # decode kernel (T <= 32, or T <= 64 with K >= 12288), else 64x64 tiles (33-64 tokens)
+    (1, 1, 16), (1, 40, 64), (5, 129, 80), (16, 1000, 256), (17, 77, 1040), (32, 300, 528), (33, 64, 48),
+    (64, 300, 528), (48, 28672, 80), (33, 136, 12288), (64, 72, 12304),
     # prefill kernel, 64x64 tiles (< 256 tiles of 128x128; 256-byte K stages), ragged
     # edges and K tails; one, two, three and more stages
     (65, 40, 16), (100, 129, 64), (300, 1000, 80), (100, 129, 304), (65, 40, 688), (257, 513, 1040),

@@ -755,6 +755,12 @@ static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st, int ncu = 0) {
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
+  // Up to 64 tokens (the shapes the decode kernel does not take): one 64-token
+  // tile reads every weight tile once, so 64x64 tiles, whatever the layer's width.
+  if (a.T <= 64) {
+    if (a.f8) return gemm_cfg<64, 64, 256, 2, 2, 2, true>(a, st);
+    return gemm_cfg<64, 64, 256, 2, 2, 2>(a, st);
+  }
   if (a.f8) {
     // 8 waves of 64 x 128: the FP8 step's 8-register operands and their
     // second slot need ~240 registers per wave, more than the 16-wave tile allows.

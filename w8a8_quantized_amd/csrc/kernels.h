@@ -79,6 +79,14 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st);
 // Any shape and alignment (one thread per output, scalar loads).
 hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st);
 
-constexpr int64_t kDecodeMaxT = 64;
+// Whether the C ABI sends a GEMM to the decode kernel rather than the tiled one.
+// Up to 32 tokens always.  From 33 to 64 tokens the tiled GEMM with 64x64 tiles
+// was faster on layers up to K = 11008 (28672 x 8192 at 48 tokens: 47.2 against
+// 51.8 us; 4096 x 4096: 15.8 against 18.8 us), while on deeper layers the decode
+// kernel, which splits K over two waves, kept the lead (8192 x 28672 at 33 tokens:
+// 89.5 against 95.9 us).
+inline bool use_decode_kernel(int64_t T, int64_t K) {
+  return T <= 32 || (T <= 64 && K >= 12288);
+}
 
 }  // namespace sq
