@@ -38,10 +38,12 @@ def _case(seed, T, K, N, dtype):
     return X, W, s
 
 
-# T <= 32 with K % 16 == 0 takes the decode kernel (16 or 32 tokens per block);
-# 33 to 64 tokens take 64x64 tiles
+# K % 16 == 0 takes the decode kernel up to 32 tokens, and up to 64 on layers of
+# at most 32 channels per CU or K >= 12288 (16, 32 or 64 tokens per block; 16, 32
+# or 64 channels per workgroup); else 64x64 tiles
 SHAPES = [(1, 8, 16), (16, 300, 512), (70, 200, 1040), (300, 520, 2048), (33, 64, 133), (257, 264, 4096),
-          (24, 100, 2048), (32, 264, 1024), (64, 264, 1024), (5, 72, 8208)]
+          (24, 100, 2048), (32, 264, 1024), (64, 264, 1024), (5, 72, 8208), (48, 6200, 272), (9, 8200, 272),
+          (24, 9000, 400), (20, 8180, 272), (40, 10240, 208), (16, 12300, 96)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -9,8 +9,9 @@
 //   * loads run D chunks ahead in a register ring, so several chunks per wave are
 //     in flight;
 //   * a workgroup owns NB*16 output channels; its KW waves take alternate K
-//     chunks (KW = 2 measured equal to or up to ~2% faster than 1 depending on the
-//     GPU, 4 clearly slower), then add their int32 partial sums exactly through
+//     chunks (on layers that fill the CUs KW = 2 measured equal to or up to ~2%
+//     faster than 1 depending on the GPU and 4 clearly slower; where each CU holds
+//     a single workgroup 4 is faster), then add their int32 partial sums exactly through
 //     LDS; each wave re-reads the small activation codes (L2-resident) once per
 //     chunk for all of its channels;
 //   * the epilogue's scale factors, and the decomposition's outlier operands
@@ -397,9 +398,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 
 constexpr size_t kGemvOutlierLds = 64 * 1024;
 
-template <int NB, int TB, bool F8>
+template <int NB, int TB, int KW, bool F8>
 static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
-  constexpr int KW = 2;
   // split N so that one launch's weight slice spans < 2^31 bytes (32-bit offsets)
   const int64_t lim = (int64_t)1 << 31;
   const int64_t n_chunk = ((lim / a.K - 16 * NB) / (16 * NB)) * (16 * NB);
@@ -427,10 +427,12 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
     } else {
       switch (a.out) {
         case kOutF32:
-          if (outl) SQ_GEMV_LAUNCH(kOutF32, true); else SQ_GEMV_LAUNCH(kOutF32, false);
+          if constexpr (KW <= 2) { if (outl) SQ_GEMV_LAUNCH(kOutF32, true); else SQ_GEMV_LAUNCH(kOutF32, false); }
+          else { if (outl) return hipErrorInvalidValue; SQ_GEMV_LAUNCH(kOutF32, false); }
           break;
         case kOutBF16:
-          if (outl) SQ_GEMV_LAUNCH(kOutBF16, true); else SQ_GEMV_LAUNCH(kOutBF16, false);
+          if constexpr (KW <= 2) { if (outl) SQ_GEMV_LAUNCH(kOutBF16, true); else SQ_GEMV_LAUNCH(kOutBF16, false); }
+          else { if (outl) return hipErrorInvalidValue; SQ_GEMV_LAUNCH(kOutBF16, false); }
           break;
         default:
           SQ_GEMV_LAUNCH(kOutI32, false);
@@ -444,20 +446,41 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
   return hipSuccess;
 }
 
+template <int NB, int KW, bool F8>
+static hipError_t gemv_tokens(const GemmArgs& a, hipStream_t st) {
+  if (a.T <= 16) return gemv_cfg<NB, 1, KW, F8>(a, st);
+  if (a.T <= 32) return gemv_cfg<NB, 2, KW, F8>(a, st);
+  return gemv_cfg<NB, 4, KW, F8>(a, st);
+}
+
 hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
-  (void)ncu;
-  // 64 channels per workgroup at every token count: with 32 (the register ring
-  // holds each chunk's token codes for every 16-token block) 17-64 tokens ran
-  // 16-29% slower (28672 x 8192: 54.7 against 45.1 us at 32 tokens, 82.1 against
-  // 57.9 us at 64; the larger ring fits in the AGPRs at one wave per SIMD)
-  if (a.f8) {
-    if (a.T <= 16) return gemv_cfg<4, 1, true>(a, st);
-    if (a.T <= 32) return gemv_cfg<4, 2, true>(a, st);
-    return gemv_cfg<4, 4, true>(a, st);
-  }
-  if (a.T <= 16) return gemv_cfg<4, 1, false>(a, st);
-  if (a.T <= 32) return gemv_cfg<4, 2, false>(a, st);
-  return gemv_cfg<4, 4, false>(a, st);
+  // Channels per workgroup (16 NB) and K-split waves (KW), by layer width; all
+  // choices give identical int8 results (exact integer partial sums), and FP8
+  // keeps two waves so that its binary32 partial sums are added in one order.
+  // Layers of 3/4 of a 64-channel block per CU or more: 64 channels, 2 waves (with
+  // 32 channels the register ring holds each chunk's token codes for every
+  // 16-token block, and 17-64 tokens ran 16-29% slower: 28672 x 8192 54.7
+  // against 45.1 us at 32 tokens; the larger ring fits in the AGPRs at one wave
+  // per SIMD).  Narrower layers spread their channels over the CUs instead:
+  // 16 channels per workgroup while that leaves at least one workgroup per CU
+  // and the token codes re-read per workgroup stay small, else 32.  Measured
+  // with the weights streamed from HBM, against 64 channels and 2 waves:
+  // 4096 x 8192 at 16 tokens 9.9 against 17.6 us (16 channels, 4 waves), 8192 x
+  // 8192 14.9 against 19.2 us (16 channels), 8192 x 28672 at 64 tokens 73.5
+  // against 95.3 us (32 channels), 6144 x 4096 at 64 tokens 14.3 against 19.9 us.
+  const bool outl = a.n_o > 0 && a.out != kOutI32;
+  const int64_t c64 = (a.N + 63) / 64, c32 = (a.N + 31) / 32;
+  // 32-channel workgroups above 16 tokens only where they make at most one round
+  // on the CUs: 10240 x 8192 at 32 tokens 29.3 us with 320 of them, 26.7 with
+  // 160 of 64 channels
+  if (4 * c64 >= 3 * (int64_t)ncu || (c32 > ncu && a.T > 16))
+    return a.f8 ? gemv_tokens<4, 2, true>(a, st) : gemv_tokens<4, 2, false>(a, st);
+  const bool nb2 = c32 >= ncu ? a.T > 16 : (4 * c32 >= 3 * (int64_t)ncu && a.T > 32);
+  if (nb2) return a.f8 ? gemv_tokens<2, 2, true>(a, st) : gemv_tokens<2, 2, false>(a, st);
+  if (a.f8) return gemv_tokens<1, 2, true>(a, st);
+  // four waves while each CU holds a single workgroup (outlier term: two)
+  if (c32 < ncu && !outl) return gemv_tokens<1, 4, false>(a, st);
+  return gemv_tokens<1, 2, false>(a, st);
 }
 
 }  // namespace sq

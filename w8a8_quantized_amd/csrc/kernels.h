@@ -81,12 +81,14 @@ hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st);
 
 // Whether the C ABI sends a GEMM to the decode kernel rather than the tiled one.
 // Up to 32 tokens always.  From 33 to 64 tokens the tiled GEMM with 64x64 tiles
-// was faster on layers up to K = 11008 (28672 x 8192 at 48 tokens: 47.2 against
-// 51.8 us; 4096 x 4096: 15.8 against 18.8 us), while on deeper layers the decode
-// kernel, which splits K over two waves, kept the lead (8192 x 28672 at 33 tokens:
-// 89.5 against 95.9 us).
-inline bool use_decode_kernel(int64_t T, int64_t K) {
-  return T <= 32 || (T <= 64 && K >= 12288);
+// was faster on layers wider than 32 channels per CU and up to K = 11008 (10240 x
+// 8192 at 48 tokens: 29.9 against 31.5 us; 28672 x 8192: 47.2 against 51.8 us);
+// the decode kernel kept the lead on narrower layers, where it spreads the
+// channels over all CUs (8192 x 8192: 24.1-24.7 against 29.5-30.0 us; 4096 x 4096:
+// 10.6-12.1 against 15.5-15.6 us), and on deeper ones, where it splits K over two
+// waves (8192 x 28672 at 33 tokens: 89.5 against 95.9 us).
+inline bool use_decode_kernel(int64_t T, int64_t N, int64_t K, int ncu) {
+  return T <= 32 || (T <= 64 && (K >= 12288 || (N + 31) / 32 <= ncu));
 }
 
 }  // namespace sq

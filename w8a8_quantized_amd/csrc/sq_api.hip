@@ -58,7 +58,7 @@ sq_status run_gemm(const int8_t* Xq, const float* xs, const int8_t* Wq, const fl
   a.vec_store = (N % 4 == 0) && aligned16(Y) && (y_t == SQ_I32 || aligned16(ws));
   const bool mfma_ok = (K % 16 == 0) && aligned16(Xq) && aligned16(Wq);
   if (!mfma_ok) return hip_status(sq::launch_gemm_generic(a, st));
-  if (sq::use_decode_kernel(T, K)) return hip_status(sq::launch_gemv_mfma(a, cu_count(), st));
+  if (sq::use_decode_kernel(T, N, K, cu_count())) return hip_status(sq::launch_gemv_mfma(a, cu_count(), st));
   return hip_status(sq::launch_gemm_mfma(a, cu_count(), st));
 }
 
