@@ -455,8 +455,9 @@ static hipError_t gemv_tokens(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // Channels per workgroup (16 NB) and K-split waves (KW), by layer width; all
-  // choices give identical int8 results (exact integer partial sums), and FP8
-  // keeps two waves so that its binary32 partial sums are added in one order.
+  // choices give identical int8 results (exact integer partial sums); for FP8 the
+  // number of waves sets the order in which binary32 partial sums are added, so
+  // two and four waves differ in the last bits, within the same error bound.
   // Layers of 3/4 of a 64-channel block per CU or more: 64 channels, 2 waves (with
   // 32 channels the register ring holds each chunk's token codes for every
   // 16-token block, and 17-64 tokens ran 16-29% slower: 28672 x 8192 54.7
@@ -477,9 +478,9 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
     return a.f8 ? gemv_tokens<4, 2, true>(a, st) : gemv_tokens<4, 2, false>(a, st);
   const bool nb2 = c32 >= ncu ? a.T > 16 : (4 * c32 >= 3 * (int64_t)ncu && a.T > 32);
   if (nb2) return a.f8 ? gemv_tokens<2, 2, true>(a, st) : gemv_tokens<2, 2, false>(a, st);
-  if (a.f8) return gemv_tokens<1, 2, true>(a, st);
   // four waves while each CU holds a single workgroup (outlier term: two)
-  if (c32 < ncu && !outl) return gemv_tokens<1, 4, false>(a, st);
+  if (c32 < ncu && !outl) return a.f8 ? gemv_tokens<1, 4, true>(a, st) : gemv_tokens<1, 4, false>(a, st);
+  if (a.f8) return gemv_tokens<1, 2, true>(a, st);
   return gemv_tokens<1, 2, false>(a, st);
 }
 
