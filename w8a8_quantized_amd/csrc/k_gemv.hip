@@ -476,6 +476,13 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // 160 of 64 channels
   if (4 * c64 >= 3 * (int64_t)ncu || (c32 > ncu && a.T > 16))
     return a.f8 ? gemv_tokens<4, 2, true>(a, st) : gemv_tokens<4, 2, false>(a, st);
+  // Deep layers of 24 to 32 channels per CU: 32 channels per workgroup, 8 waves up
+  // to 32 tokens and 4 above (8192 x 28672 at 1/16/32/48/64 tokens
+  // 37.8/40.5/49.2/61.7/70.5 us against 41.5/46.7/54.1/69.9/73.5)
+  if (a.K >= 16384 && !outl && c32 <= ncu && 4 * c32 >= 3 * (int64_t)ncu) {
+    if (a.T <= 32) return a.f8 ? gemv_tokens<2, 8, true>(a, st) : gemv_tokens<2, 8, false>(a, st);
+    return a.f8 ? gemv_tokens<2, 4, true>(a, st) : gemv_tokens<2, 4, false>(a, st);
+  }
   const bool nb2 = c32 >= ncu ? a.T > 16 : (4 * c32 >= 3 * (int64_t)ncu && a.T > 32);
   if (nb2) return a.f8 ? gemv_tokens<2, 2, true>(a, st) : gemv_tokens<2, 2, false>(a, st);
   // four waves while each CU holds a single workgroup (outlier term: two)
