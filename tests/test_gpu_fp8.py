@@ -44,7 +44,7 @@ def _case(seed, T, K, N, dtype):
 SHAPES = [(1, 8, 16), (16, 300, 512), (70, 200, 1040), (300, 520, 2048), (33, 64, 133), (257, 264, 4096),
           (24, 100, 2048), (32, 264, 1024), (64, 264, 1024), (5, 72, 8208), (48, 6200, 272), (9, 8200, 272),
           (24, 9000, 400), (20, 8180, 272), (40, 10240, 208), (16, 12300, 96),
-          (9, 8192, 16384), (40, 6200, 16400)]
+          (9, 8192, 16384), (40, 6200, 16400), (9, 12300, 8208)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

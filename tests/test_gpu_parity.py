@@ -169,7 +169,7 @@ GEMM_SHAPES = [
     (1, 1, 16), (1, 40, 64), (5, 129, 80), (16, 1000, 256), (17, 77, 1040), (32, 300, 528), (33, 64, 48),
     (64, 300, 528), (48, 28672, 80), (33, 136, 12288), (64, 72, 12304), (40, 4100, 1040), (64, 6200, 528),
     (20, 6200, 272), (9, 8200, 272), (24, 9000, 400), (20, 8180, 272), (33, 8192, 208), (48, 10240, 208), (16, 12300, 96),
-    (3, 8192, 16384), (20, 6200, 16400), (40, 8192, 16384),
+    (3, 8192, 16384), (20, 6200, 16400), (40, 8192, 16384), (5, 12300, 8192), (16, 16000, 8208),
     # prefill kernel, 64x64 tiles (< 256 tiles of 128x128; 256-byte K stages), ragged
     # edges and K tails; one, two, three and more stages
     (65, 40, 16), (100, 129, 64), (300, 1000, 80), (100, 129, 304), (65, 40, 688), (257, 513, 1040),
