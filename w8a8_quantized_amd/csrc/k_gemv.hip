@@ -457,7 +457,7 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // Channels per workgroup (16 NB) and K-split waves (KW), by layer width; all
   // choices give identical int8 results (exact integer partial sums); for FP8 the
   // number of waves sets the order in which binary32 partial sums are added, so
-  // two and four waves differ in the last bits, within the same error bound.
+  // different wave counts differ in the last bits, within the same error bound.
   // Layers of 3/4 of a 64-channel block per CU or more: 64 channels, 2 waves (with
   // 32 channels the register ring holds each chunk's token codes for every
   // 16-token block, and 17-64 tokens ran 16-29% slower: 28672 x 8192 54.7
@@ -471,14 +471,14 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // against 95.3 us (32 channels), 6144 x 4096 at 64 tokens 14.3 against 19.9 us.
   const bool outl = a.n_o > 0 && a.out != kOutI32;
   const int64_t c64 = (a.N + 63) / 64, c32 = (a.N + 31) / 32;
-  // 32-channel workgroups above 16 tokens only where they make at most one round
-  // on the CUs: 10240 x 8192 at 32 tokens 29.3 us with 320 of them, 26.7 with
-  // 160 of 64 channels
   // Layers of 3/4 to one 64-channel block per CU, K >= 8192, up to 16 tokens:
   // 8 waves (12288 x 12288 at 1/16 tokens 27.6/30.0 against 32.2/33.7 us,
   // 12288 x 49152 94.4/103.2 against 105.3/112.3; at 28672 channels 8 waves lost)
   if (4 * c64 >= 3 * (int64_t)ncu && c64 < ncu && a.K >= 8192 && a.T <= 16 && !outl)
     return a.f8 ? gemv_cfg<4, 1, 8, true>(a, st) : gemv_cfg<4, 1, 8, false>(a, st);
+  // 32-channel workgroups above 16 tokens only where they make at most one round
+  // on the CUs: 10240 x 8192 at 32 tokens 29.3 us with 320 of them, 26.7 with
+  // 160 of 64 channels
   if (4 * c64 >= 3 * (int64_t)ncu || (c32 > ncu && a.T > 16))
     return a.f8 ? gemv_tokens<4, 2, true>(a, st) : gemv_tokens<4, 2, false>(a, st);
   // Deep layers of 24 to 32 channels per CU: 32 channels per workgroup, 8 waves up
