@@ -37,7 +37,7 @@ __all__ = ["build", "col_absmax", "smooth_scales", "quantize_weights", "quant_ac
            "quant_act_per_tensor", "fold_gain", "norm_stats", "norm_apply", "norm_quant_act",
            "decomp_select", "decomp_split", "decomp_outlier_product", "decomp_prepare",
            "decomp_linear", "decomp_relative_error", "e4m3_encode", "e4m3_decode",
-           "quantize_weights_fp8", "quant_act_fp8", "fp8_dot_at", "fp8_relative_error"]
+           "quantize_weights_fp8", "quant_act_fp8", "fp8_dot_at", "fp8_dot", "fp8_relative_error"]
 
 GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
              "-std=c11", "-Wall"]
@@ -372,6 +372,31 @@ def fp8_dot_at(Xq, Wq, ti, ni):
     sab = np.empty(ti.size, np.float64)
     _load().sqo_fp8_dot_at(_ptr(Xq), _ptr(Wq), Xq.shape[1], _ptr(ti), _ptr(ni), ti.size, _ptr(acc),
                            _ptr(sab))
+    return acc, sab
+
+
+def fp8_dot(Xq, Wq, rows=2048):
+    """Exact dot products of decoded E4M3 codes for every (t, n), and the sums of
+    |products| ([P3] formats paragraph: the FP8 layer's accumulator is the sum of
+    the code products).  Computed as binary64 matrix products of the decoded
+    codes, `rows` tokens at a time.  That is exact in any summation order: every
+    E4M3 value is a multiple of 2^-9 with |v| <= 448, so every product is a
+    multiple of 2^-18 below 2^18 in magnitude, and for K <= 2^16 every partial
+    sum is a multiple of 2^-18 below 2^34, which binary64 holds exactly; the
+    library product therefore gives the same values as fp8_dot_at's loop."""
+    Xq = np.ascontiguousarray(Xq, np.uint8)
+    Wq = np.ascontiguousarray(Wq, np.uint8)
+    assert Xq.shape[1] == Wq.shape[1] and Xq.shape[1] <= 1 << 16
+    lut = e4m3_decode(np.arange(256)).astype(np.float64)
+    wv = lut[Wq].T.copy()
+    wa = np.abs(wv)
+    T, N = Xq.shape[0], Wq.shape[0]
+    acc = np.empty((T, N), np.float64)
+    sab = np.empty((T, N), np.float64)
+    for t0 in range(0, T, rows):
+        xv = lut[Xq[t0:t0 + rows]]
+        acc[t0:t0 + rows] = xv @ wv
+        sab[t0:t0 + rows] = np.abs(xv) @ wa
     return acc, sab
 
 

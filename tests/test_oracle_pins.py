@@ -715,3 +715,25 @@ def test_fp8_dot_is_exact():
     exact = (xi[ti] * wi[ni]).sum(1)
     assert np.array_equal(acc * 2.0 ** 18, exact.astype(np.float64))
     assert np.array_equal(sab * 2.0 ** 18, np.abs(xi[ti] * wi[ni]).sum(1).astype(np.float64))
+
+
+def test_fp8_dot_full_matches_brute_force():
+    """The full-matrix form (binary64 library product) equals the per-pair loop
+    and pure-Python integer arithmetic on the codes, over the whole code range
+    (subnormals, both signs, 448), with K long enough to cross row blocks."""
+    rng = np.random.default_rng(59)
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    Xq = rng.choice(codes, (9, 1100)).astype(np.uint8)
+    Wq = rng.choice(codes, (6, 1100)).astype(np.uint8)
+    Xq[0, :] = 0x7E                      # 448 everywhere: the largest products
+    Wq[0, :] = 0x7E
+    acc, sab = O.fp8_dot(Xq, Wq, rows=4)
+    ti, ni = np.repeat(np.arange(9), 6), np.tile(np.arange(6), 9)
+    acc_p, sab_p = O.fp8_dot_at(Xq, Wq, ti, ni)
+    assert np.array_equal(acc[ti, ni], acc_p) and np.array_equal(sab[ti, ni], sab_p)
+    dec = {c: O.e4m3_decode(np.array([c], np.uint8))[0] for c in range(256)}
+    for t, n in ((0, 0), (3, 5), (8, 2)):
+        # each decoded value times 2^9 is an integer, so this is exact
+        ints = [int(dec[int(a)] * 512) * int(dec[int(b)] * 512) for a, b in zip(Xq[t], Wq[n])]
+        assert acc[t, n] * 2.0 ** 18 == float(sum(ints))
+        assert sab[t, n] * 2.0 ** 18 == float(sum(abs(v) for v in ints))
