@@ -105,8 +105,11 @@ def _draw_outliers(rng, K, n_out, mult_range):
     return idx, mult
 
 
-def _acts(rng, T, K, idx, mult):
-    X = rng.standard_normal((T, K), dtype=np.float32)
+def _acts(rng, T, K, dtype):
+    return rng.standard_normal((T, K), dtype=dtype)
+
+
+def _plant(X, idx, mult):
     if len(idx):
         X[:, idx] *= mult[None, :]
     return X
@@ -114,22 +117,30 @@ def _acts(rng, T, K, idx, mult):
 
 def make_linear(T, N, K, *, n_out=0, mult_range=(60.0, 60.0), seed=0, x_dtype="f32",
                 y_dtype="f32", alphas=(0.5,), calib_tokens=None, w_std=0.02,
-                name=None) -> Workload:
+                name=None, draw_dtype=np.float32, channels_after_acts=False) -> Workload:
     """Generic seeded outlier-structured linear problem (any shape).
 
     Order of draws from numpy's PCG64 stream seeded with `seed`: outlier channel
-    indices, multipliers, activations [T, K], weights [N, K].  The calibration
-    draw, when asked for, uses its own stream seeded with seed + 100.
+    indices, multipliers, activations [T, K], weights [N, K]; with
+    channels_after_acts the activations come first.  The calibration draw, when
+    asked for, uses its own stream seeded with seed + 100.  draw_dtype float64
+    keeps the draw (and X, W) in float64 instead of float32; such a draw is
+    used as float64 data (x_dtype must stay "f32").
     """
     rng = np.random.default_rng(seed)
-    idx, mult = _draw_outliers(rng, K, n_out, mult_range)
-    X = _acts(rng, T, K, idx, mult)
-    W = rng.standard_normal((N, K), dtype=np.float32)
-    W *= np.float32(w_std)
+    if channels_after_acts:
+        X = _acts(rng, T, K, draw_dtype)
+        idx, mult = _draw_outliers(rng, K, n_out, mult_range)
+    else:
+        idx, mult = _draw_outliers(rng, K, n_out, mult_range)
+        X = _acts(rng, T, K, draw_dtype)
+    X = _plant(X, idx, mult)
+    W = rng.standard_normal((N, K), dtype=draw_dtype)
+    W *= W.dtype.type(w_std)
     Xc = None
     if calib_tokens:
-        Xc = _acts(np.random.default_rng(seed + 100), calib_tokens, K, idx, mult)
-    if x_dtype == "bf16":
+        Xc = _plant(_acts(np.random.default_rng(seed + 100), calib_tokens, K, draw_dtype), idx, mult)
+    if x_dtype == "bf16" and draw_dtype == np.float32:
         X = _round_bf16(X)
         if Xc is not None:
             Xc = _round_bf16(Xc)
@@ -177,15 +188,14 @@ def make(name: str, *, tokens: Optional[int] = None) -> Workload:
 def page3_experiment_data():
     """The synthetic data of the NumPy experiment on inferenceinterviews.com,
     "Why do activation outliers break INT8 W8A8..." (section "A strong answer"):
-    numpy default_rng(0); activations 512 x 4096 standard normal; 6 distinct
-    channels drawn without replacement and multiplied by 60; weights
-    1024 x 4096 standard normal times 0.02.  Values are float64 as drawn."""
-    rng = np.random.default_rng(0)
-    X = rng.normal(size=(512, 4096))
-    cols = rng.choice(4096, 6, replace=False)
-    X[:, cols] *= 60
-    W = rng.normal(size=(1024, 4096)) * 0.02
-    return X, W, np.sort(cols)
+    seed 0; 512 tokens x 4096 channels, standard normal; 6 distinct channels
+    multiplied by 60 in every token; 1024 output channels, standard normal
+    weights times 0.02.  The printed figures depend on the exact stream, so the
+    draw is made in float64 with the channels chosen after the activations, in
+    the experiment's order.  Returns (X, W, outlier channels), float64."""
+    w = make_linear(512, 1024, 4096, n_out=6, mult_range=(60.0, 60.0), seed=0,
+                    draw_dtype=np.float64, channels_after_acts=True, name="page3_experiment")
+    return w.X, w.W, w.outliers
 
 
 def page_tiny_fixture(seed=7, T=37, N=45, K=80):
