@@ -133,7 +133,7 @@ def test_decomp_generic_gemm_path(sq):
 def test_decomp_full_size(sq, name, n_o):
     """The decode and prefill workloads with their planted channel count taken as
     the static outlier set, chosen from the calibration draw: the chosen set,
-    codes and scales in full; outputs in full (decode) or on sampled pairs."""
+    codes, scales, bulk accumulators and outputs, all in full."""
     w = WL.make(name)
     a = O.col_absmax(w.X_calib)
     idx, mask = sq.sq_decomp_select(torch.from_numpy(a).to(DEV), n_o)
@@ -148,14 +148,6 @@ def test_decomp_full_size(sq, name, n_o):
     Xq_r, xs_r = O.quant_act(Xb, None)
     _check_split(host(Xq), host(xs), host(Xo), Xq_r, xs_r, Xo_r, idx_h)
     y = host(sq.sq_decomp_gemm(Xq, xs, Wq, ws, Xo, Wo, out_dtype=torch.bfloat16))
-    yo = O.decomp_outlier_product(Xo_r, Wo_r)
-    if w.T <= 64:
-        y_r, *_ = O.decomp_linear(w.X, idx_h, Wq_r, ws_r, Wo_r)
-        assert_out_close(y, y_r, "bf16")
-    else:
-        rng = np.random.default_rng(3)
-        ti, ni = rng.integers(0, w.T, 100_000), rng.integers(0, w.N, 100_000)
-        acc = O.int_gemm_at(Xq_r, Wq_r, ti, ni)
-        yb = O.dequant_at(acc, xs_r, ws_r, ti, ni)
-        y_r = (yb + yo[ti, ni]).astype(np.float32)
-        assert_out_close(y[ti, ni], y_r, "bf16")
+    y_r, _, _, _, acc_r = O.decomp_linear(w.X, idx_h, Wq_r, ws_r, Wo_r)
+    assert np.array_equal(host(sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32)), acc_r)
+    assert_out_close(y, y_r, "bf16")

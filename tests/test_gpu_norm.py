@@ -55,8 +55,18 @@ def _check(sq, X, dtype, kind, g, b, eps, Xd=None):
     same = (mean == mean_r) & (rstd == rstd_r)
     Xq_o, xs_o, _, _ = O.norm_quant_act(X, kind, g, b, eps=eps)
     assert np.array_equal(Xq[same], Xq_o[same]) and np.array_equal(xs[same], xs_o[same])
-    if same.size >= 32:
-        assert same.mean() > 0.5      # most rows' statistics round like the oracle's
+    # The kernel sums each 8-element chunk of squares in binary32 with fused
+    # multiply-adds (chunk sums in binary64): for non-negative terms the mean
+    # square is then within 8 * 2^-24 relative of the binary64 one (LayerNorm:
+    # 10 * 2^-24, its centred differences being rounded once more), so rstd is
+    # within half of that before its final rounding, and the two rounded values
+    # differ by at most that plus one binary32 ulp.  Rows whose binary64 value
+    # lies that close to a rounding boundary round apart; with few chunks per row
+    # (short K) that can be most rows, so no share of equal rows is asserted.
+    delta = (5.0 if kind == "layer" else 4.0) * 2.0 ** -24
+    r64 = rstd_r.astype(np.float64)
+    ulp = np.spacing(np.abs(rstd_r)).astype(np.float64)
+    assert np.all(np.abs(rstd.astype(np.float64) - r64) <= delta * r64 + ulp)
     return Xq, xs
 
 

@@ -68,6 +68,40 @@ def test_smooth_scales_dtypes(sq, xdt, wdt, T, N, K):
     assert np.array_equal(host(xa2), xa_r) and np.array_equal(host(wa2), wa_r)
 
 
+@pytest.mark.parametrize("xdt,wdt", [("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("T,N,K", [(1, 1, 8), (37, 300, 1000), (600, 5, 4096), (40, 60, 83), (70, 2100, 8192)])
+@pytest.mark.parametrize("maxima", [(False, True), (True, False), (False, False)])
+def test_smooth_scales_without_maxima_outputs(sq, xdt, wdt, T, N, K, maxima):
+    """x_absmax and/or w_absmax passed as NULL: the same factors, bit for bit, as
+    with both outputs (vector and scalar forms of the in-workgroup weight maxima,
+    ragged K), and the oracle's within 1e-6; alpha 0 and 1 exactly."""
+    rng = np.random.default_rng(T * 3 + N + K)
+    X = (rng.standard_normal((T, K)) * rng.uniform(0.1, 40, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, K // 2] = 0.0                     # a zero weight column: the 1e-8 floor
+    X[T // 2, K // 3] = -900.0
+    if xdt == "bf16":
+        X = bf16_round(X)
+    if wdt == "bf16":
+        W = bf16_round(W)
+    Xd, Wd = dev_act(X, xdt), dev_act(W, wdt)
+    for alpha in (0.0, 0.5, 1.0):
+        s_ref, xa, wa = sq.sq_smooth_scales(Xd, Wd, alpha)
+        s, xa2, wa2 = sq.sq_smooth_scales(Xd, Wd, alpha, maxima=maxima)
+        assert np.array_equal(host(s), host(s_ref))
+        if maxima[0]:
+            assert np.array_equal(host(xa2), host(xa))
+        if maxima[1]:
+            assert np.array_equal(host(wa2), host(wa))
+        s_r = O.smooth_scales(O.col_absmax(X), O.col_absmax(W), alpha)
+        np.testing.assert_allclose(host(s), s_r, rtol=1e-6, atol=0)
+        if alpha in (0.0, 1.0):
+            assert np.array_equal(host(s), s_r)
+        # the scalar kernels (misaligned rows) give the same bits
+        s3, _, _ = sq.sq_smooth_scales(misaligned(Xd), misaligned(Wd), alpha, maxima=maxima)
+        assert np.array_equal(host(s3), host(s_ref))
+
+
 @pytest.mark.parametrize("alpha", [0.0, 0.25, 0.5, 0.75, 1.0])
 def test_smooth_scales(sq, alpha):
     w = WL.page_tiny_fixture(seed=3, T=50, N=70, K=96)
@@ -203,8 +237,22 @@ def test_gemm_int32_accumulators(sq, T, N, K):
     assert np.array_equal(host(acc), O.int_gemm(Xq, Wq))
 
 
+def test_decode_shapes_assume_256_cus(sq):
+    """The decode shapes above reach the 4- and 8-wave and 32-channel forms of the
+    decode kernel only on a GPU with 256 compute units (the forms are chosen by
+    how many workgroups fill the CUs); on another CU count they would silently
+    test other forms, so that is reported here."""
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("T,N,K", [(1, 40, 64), (17, 77, 1040), (300, 1000, 80), (2100, 8200, 48),
+                                   # decode forms: 8 K-split waves (12288 <= N < 16384,
+                                   # K >= 8192, <= 16 tokens); 32 channels with 8 or 4
+                                   # waves (K >= 16384, 6144 <= N <= 8192); 32 channels
+                                   # with 2 waves (N = 8192, 17-64 tokens)
+                                   (5, 12300, 8192), (16, 16000, 8208), (3, 8192, 16384),
+                                   (40, 8192, 16384), (20, 6200, 16400), (33, 8192, 208),
                                    (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272),
                                    (100, 129, 688), (1000, 4100, 608), (2100, 8200, 336),
                                    (100, 12800, 208), (65, 14336, 656), (768, 16384, 208),
@@ -317,23 +365,13 @@ def test_linear_tiny_and_page(sq, alpha):
         assert_out_close(host(y), O.dequant(acc_r, xs_r, ws_r), "f32")
 
 
-def _sampled_pairs(rng, T, N, count):
-    ti = rng.integers(0, T, count)
-    ni = rng.integers(0, N, count)
-    # whole first/last rows and columns, and tile corners
-    edge_t = np.concatenate([np.zeros(N, np.int64), np.full(N, T - 1)])
-    edge_n = np.concatenate([np.arange(N), np.arange(N)])
-    col_t = np.concatenate([np.arange(T), np.arange(T)])
-    col_n = np.concatenate([np.zeros(T, np.int64), np.full(T, N - 1)])
-    return np.concatenate([ti, edge_t, col_t]), np.concatenate([ni, edge_n, col_n])
-
-
 @pytest.mark.parametrize("name", ["decode_t16_k8192_n28672", "prefill_t2048_k4096_n16384",
                                   "heavy_t8192_k8192_n8192"])
 def test_linear_full_size(sq, name):
-    """Full-size workloads in the configuration the benchmark times: codes and
-    scales compared in full, accumulators and outputs on sampled (t, n) pairs
-    (all of them for the 16-token decode shape)."""
+    """Full-size workloads in the configuration the benchmark times: codes,
+    scales, every int32 accumulator and every bf16 output compared in full with
+    the oracle (the heavy 8192^3 product is ~5.5e11 integer multiply-adds of the
+    oracle's loop)."""
     w = WL.make(name)
     alpha = w.alpha
     s, xa, wa, Wq, ws = _prepare_gpu(sq, w, alpha)
@@ -345,19 +383,13 @@ def test_linear_full_size(sq, name):
     assert np.array_equal(host(xs), xs_r)
     assert np.array_equal(host(Xq), Xq_r)
     yh = host(y)
-    if w.T <= 64:
-        acc_r = O.int_gemm(Xq_r, Wq_r)
-        acc = host(sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32))
-        assert np.array_equal(acc, acc_r)
-        assert_out_close(yh, O.dequant(acc_r, xs_r, ws_r), "bf16")
-    else:
-        rng = np.random.default_rng(42)
-        ti, ni = _sampled_pairs(rng, w.T, w.N, 200_000)
-        acc_r = O.int_gemm_at(Xq_r, Wq_r, ti, ni)
-        acc = host(sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32))
-        assert np.array_equal(acc[ti, ni], acc_r)
-        y_r = O.dequant_at(acc_r, xs_r, ws_r, ti, ni)
-        assert_out_close(yh[ti, ni], y_r, "bf16")
+    acc = host(sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=torch.int32))
+    acc_r = O.int_gemm(Xq_r, Wq_r)
+    bad = np.argwhere(acc != acc_r)
+    assert bad.size == 0, f"{len(bad)} accumulators differ, first at (t, n) = {bad[:4].tolist()}"
+    del acc
+    assert_out_close(yh, O.dequant(acc_r, xs_r, ws_r), "bf16")
+    del acc_r
     # the W8A8 layer actually tracks the exact product (smoothing worked)
     rows = np.arange(0, w.T, max(1, w.T // 16))
     ye = O.exact_product(w.X[rows], w.W)
