@@ -105,13 +105,18 @@ sq_status sq_smooth_scales_from_absmax(const float *x_absmax, const float *w_abs
 
 /*
  * Smoothing factors from a calibration batch X [T x K] and the weights W [N x K]:
- * the two column maxima above followed by the formula above.  The maxima are
- * returned too.
+ * the two column maxima above followed by the formula above
+ * (inferenceinterviews page, "A strong answer": s_j from max over t of |X_tj|
+ * and max over n of |W_nj|).  The maxima are returned too when asked for.
  *   X         device, x_t = SQ_F32 or SQ_BF16, [T][K]
  *   W         device, w_t = SQ_F32 or SQ_BF16, [N][K]
  *   s         device float [K], written
- *   x_absmax  device float [K], written (max_t |X_tj|)
- *   w_absmax  device float [K], written (max_n |W_nj|)
+ *   x_absmax  device float [K], written (max_t |X_tj|), or NULL: the maxima
+ *             are then formed in s and replaced by the factors
+ *   w_absmax  device float [K], written (max_n |W_nj|), or NULL: each
+ *             workgroup then forms the maxima of a strip of columns over all of
+ *             W and writes those columns' factors (no buffer, fewer workgroups:
+ *             slower on wide W, the same s bit for bit)
  */
 sq_status sq_smooth_scales(const void *X, sq_dtype x_t, int64_t T,
                            const void *W, sq_dtype w_t, int64_t N, int64_t K,

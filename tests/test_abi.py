@@ -83,7 +83,8 @@ def test_null_pointers_rejected(lib):
     assert lib.sq_quant_act(None, F32, 4, 4, None, FAKE, FAKE, None) == SQ_ERR_NULL
     assert lib.sq_quant_act(FAKE, F32, 4, 4, None, None, FAKE, None) == SQ_ERR_NULL
     assert lib.sq_quantize_weights(FAKE, F32, 4, 4, None, FAKE, None, None) == SQ_ERR_NULL
-    assert lib.sq_smooth_scales(FAKE, F32, 4, FAKE, F32, 4, 4, 0.5, FAKE, None, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_smooth_scales(FAKE, F32, 4, FAKE, F32, 4, 4, 0.5, None, FAKE, FAKE, None) == SQ_ERR_NULL
+    assert lib.sq_smooth_scales(None, F32, 4, FAKE, F32, 4, 4, 0.5, FAKE, None, None, None) == SQ_ERR_NULL
     assert lib.sq_smooth_scales_from_absmax(FAKE, None, 4, 0.5, FAKE, None) == SQ_ERR_NULL
     # scales are required unless the output is the raw int32 accumulator
     assert lib.sq_w8a8_gemm(FAKE, None, FAKE, FAKE, 4, 4, 16, FAKE, F32, None) == SQ_ERR_NULL
@@ -100,6 +101,14 @@ def test_shapes_rejected(lib):
     assert lib.sq_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 16, FAKE, F32, None) == SQ_ERR_SHAPE
     assert lib.sq_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 133145, FAKE, F32, None) == SQ_ERR_SHAPE
     assert lib.sq_smooth_scales_from_absmax(FAKE, FAKE, 0, 0.5, FAKE, None) == SQ_ERR_SHAPE
+
+
+def test_smooth_scales_maxima_outputs_optional(lib):
+    """x_absmax and w_absmax may be NULL: the call gets past validation (the
+    status is then that of the next check, here alpha) instead of SQ_ERR_NULL."""
+    for xa, wa in ((None, FAKE), (FAKE, None), (None, None)):
+        assert lib.sq_smooth_scales(FAKE, F32, 4, FAKE, BF16, 4, 8, 1.5, FAKE, xa, wa, None) == SQ_ERR_ALPHA
+        assert lib.sq_smooth_scales(FAKE, F32, 0, FAKE, BF16, 4, 8, 0.5, FAKE, xa, wa, None) == SQ_ERR_SHAPE
 
 
 def test_alpha_rejected(lib):

@@ -324,13 +324,10 @@ __global__ __launch_bounds__(256) void tensor_absmax_rows_kernel(const T* __rest
 // s_j = max(xa_j, 1e-8)^alpha / max(wa_j, 1e-8)^(1 - alpha), binary64, rounded once
 // (multigrid.ai "SmoothQuant Explained", section "Alpha: how much difficulty to
 // move"; 1e-8 floor from the maitreyasuin page, section "Route it, or move it").
-__global__ void smooth_scales_kernel(const float* __restrict__ xa, const float* __restrict__ wa,
-                                     int64_t K, double alpha, float* __restrict__ s) {
-  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= K) return;
+__device__ __forceinline__ float smooth_factor(float xa, float wa, double alpha) {
   const float eps = 1e-8f;
-  const float x = xa[j] < eps ? eps : xa[j];
-  const float w = wa[j] < eps ? eps : wa[j];
+  const float x = xa < eps ? eps : xa;
+  const float w = wa < eps ? eps : wa;
   double r;
   if (alpha == 0.0) {
     r = 1.0 / (double)w;                 // the alpha = 0 form, exactly
@@ -339,7 +336,88 @@ __global__ void smooth_scales_kernel(const float* __restrict__ xa, const float* 
   } else {
     r = pow((double)x, alpha) / pow((double)w, 1.0 - alpha);
   }
-  s[j] = (float)r;
+  return (float)r;
+}
+
+// xa may alias s (each entry is read, then written, by one thread).
+__global__ void smooth_scales_kernel(const float* xa, const float* __restrict__ wa, int64_t K, double alpha,
+                                     float* s) {
+  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  s[j] = smooth_factor(xa[j], wa[j], alpha);
+}
+
+// Smoothing factors whose weight maxima are formed inside one workgroup, for
+// callers that keep no [K] buffer of weight maxima: a workgroup owns a strip of
+// columns over all N rows of W, so each column's maximum is final when its
+// waves meet in LDS, and the workgroup then writes s_j = factor(xa_j, wa_j) for
+// its columns.  Vector form (16-byte aligned rows): a strip is 128 bytes of each
+// row (32 fp32 / 64 bf16 columns); lane l reads 16-byte chunk l % 8 of row
+// l / 8 of an 8-row group, the 4 waves take successive 8-row groups, U groups of
+// loads in flight.  xa may alias s: each column is read, then written, by the
+// same thread, after every load of W.
+template <typename T, int U>
+__global__ __launch_bounds__(256) void smooth_wstrip_kernel(const T* __restrict__ W, int64_t N, int64_t K,
+                                                            const float* xa, double alpha, float* s) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int SC = 8 * VEC;   // columns per strip
+  __shared__ float part[32][SC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = lane & 7, rsub = lane >> 3;
+  const int64_t c0 = (int64_t)blockIdx.x * SC + chunk * VEC;
+  ColMax<T, VEC> acc;
+  acc.init();
+  if (c0 < K) {   // K % VEC == 0 on this path
+    const T* p = W + c0;
+    int64_t r = (int64_t)wave * 8 + rsub;
+    for (; r + 32 * (U - 1) < N; r += 32 * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc.add(p + (r + 32 * u) * K);
+    }
+    for (; r < N; r += 32) acc.add(p + r * K);
+  }
+  float m[VEC];
+  acc.result(m);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) part[wave * 8 + rsub][chunk * VEC + i] = m[i];
+  __syncthreads();
+  if (tid < SC) {
+    const int64_t j = (int64_t)blockIdx.x * SC + tid;
+    if (j < K) {
+      float w = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 32; ++g) w = fmaxf(w, part[g][tid]);
+      s[j] = smooth_factor(xa[j], w, alpha);
+    }
+  }
+}
+
+// Scalar form of the same (any alignment): lane l owns column 64 * blockIdx.x + l,
+// the 4 waves take rows wave, wave + 4, ...
+template <typename T, int U>
+__global__ __launch_bounds__(256) void smooth_wcol_kernel(const T* __restrict__ W, int64_t N, int64_t K,
+                                                          const float* xa, double alpha, float* s) {
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+  ColMax<T, 1> acc;
+  acc.init();
+  if (j < K) {
+    const T* p = W + j;
+    int64_t r = wave;
+    for (; r + 4 * (U - 1) < N; r += 4 * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc.add(p + (r + 4 * u) * K);
+    }
+    for (; r < N; r += 4) acc.add(p + r * K);
+  }
+  float m;
+  acc.result(&m);
+  part[wave][lane] = m;
+  __syncthreads();
+  if (wave == 0 && j < K)
+    s[j] = smooth_factor(xa[j], fmaxf(fmaxf(part[0][lane], part[1][lane]), fmaxf(part[2][lane], part[3][lane])),
+                         alpha);
 }
 
 static int grid_1d(int64_t n, int threads, int cap) {
@@ -485,6 +563,26 @@ hipError_t launch_tensor_absmax(const void* A, bool bf16, int64_t rows, int64_t 
                                 float* amax, bool vec_ok, int ncu, hipStream_t st) {
   if (bf16) return tensor_absmax_any(static_cast<const uint16_t*>(A), rows, cols, s, amax, vec_ok, ncu, st);
   return tensor_absmax_any(static_cast<const float*>(A), rows, cols, s, amax, vec_ok, ncu, st);
+}
+
+template <typename T>
+static hipError_t smooth_from_w_t(const T* W, int64_t N, int64_t K, const float* xa, double alpha, float* s,
+                                  bool vec_ok, hipStream_t st) {
+  if (vec_ok) {
+    constexpr int SC = 8 * (16 / sizeof(T));
+    hipLaunchKernelGGL((smooth_wstrip_kernel<T, 4>), dim3((unsigned)((K + SC - 1) / SC)), dim3(256), 0, st, W, N,
+                       K, xa, alpha, s);
+  } else {
+    hipLaunchKernelGGL((smooth_wcol_kernel<T, 8>), dim3((unsigned)((K + 63) / 64)), dim3(256), 0, st, W, N, K,
+                       xa, alpha, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_smooth_scales_from_w(const void* W, bool bf16, int64_t N, int64_t K, const float* xa,
+                                       float alpha, float* s, bool vec_ok, hipStream_t st) {
+  if (bf16) return smooth_from_w_t(static_cast<const uint16_t*>(W), N, K, xa, (double)alpha, s, vec_ok, st);
+  return smooth_from_w_t(static_cast<const float*>(W), N, K, xa, (double)alpha, s, vec_ok, st);
 }
 
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,

@@ -20,8 +20,13 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
 // wa); both with 16-byte aligned rows of a multiple of 16 bytes.
 hipError_t launch_col_absmax_pair(const void* X, bool x_bf16, int64_t T, const void* W, bool w_bf16, int64_t N,
                                   int64_t K, float* xa, float* wa, int ncu, hipStream_t st);
+// xa may alias s.
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
                                 hipStream_t st);
+// s from the column maxima xa [K] (may alias s) and W [N][K], whose column
+// maxima are formed inside the launch and not stored.
+hipError_t launch_smooth_scales_from_w(const void* W, bool bf16, int64_t N, int64_t K, const float* xa,
+                                       float alpha, float* s, bool vec_ok, hipStream_t st);
 // Row quantiser modes: per-token activations (divide by s, per-row range),
 // per-output-channel weights (multiply by s, per-row range; also the
 // decomposition's bulk weight rows, with s a 0/1 column mask), activations against

@@ -131,22 +131,32 @@ sq_status sq_smooth_scales_from_absmax(const float* x_absmax, const float* w_abs
 sq_status sq_smooth_scales(const void* X, sq_dtype x_t, int64_t T, const void* W, sq_dtype w_t,
                            int64_t N, int64_t K, float alpha, float* s, float* x_absmax,
                            float* w_absmax, hipStream_t stream) {
-  if (!X || !W || !s || !x_absmax || !w_absmax) return SQ_ERR_NULL;
+  if (!X || !W || !s) return SQ_ERR_NULL;
   if (!in_dtype(x_t) || !in_dtype(w_t)) return SQ_ERR_DTYPE;
   if (T < 1 || N < 1 || K < 1) return SQ_ERR_SHAPE;
   if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
-  if (sq::launch_fill2(x_absmax, w_absmax, K, 0.0f, stream) != hipSuccess) return SQ_ERR_HIP;
-  if (rows_vec16(X, K, esize(x_t)) && rows_vec16(W, K, esize(w_t))) {
-    if (sq::launch_col_absmax_pair(X, x_t == SQ_BF16, T, W, w_t == SQ_BF16, N, K, x_absmax, w_absmax, cu_count(),
-                                   stream) != hipSuccess)
-      return SQ_ERR_HIP;
-  } else {
-    sq_status r = sq_col_absmax(X, x_t, T, K, x_absmax, 1, stream);
-    if (r != SQ_OK) return r;
-    r = sq_col_absmax(W, w_t, N, K, w_absmax, 1, stream);
-    if (r != SQ_OK) return r;
+  // X's column maxima go to x_absmax, or to s itself when they are not asked for
+  float* xa = x_absmax ? x_absmax : s;
+  const bool vx = rows_vec16(X, K, esize(x_t)), vw = rows_vec16(W, K, esize(w_t));
+  if (w_absmax) {
+    if (sq::launch_fill2(xa, w_absmax, K, 0.0f, stream) != hipSuccess) return SQ_ERR_HIP;
+    if (vx && vw) {
+      if (sq::launch_col_absmax_pair(X, x_t == SQ_BF16, T, W, w_t == SQ_BF16, N, K, xa, w_absmax, cu_count(),
+                                     stream) != hipSuccess)
+        return SQ_ERR_HIP;
+    } else {
+      if (sq::launch_col_absmax(X, x_t == SQ_BF16, T, K, xa, vx, cu_count(), stream) != hipSuccess ||
+          sq::launch_col_absmax(W, w_t == SQ_BF16, N, K, w_absmax, vw, cu_count(), stream) != hipSuccess)
+        return SQ_ERR_HIP;
+    }
+    return hip_status(sq::launch_smooth_scales(xa, w_absmax, K, alpha, s, stream));
   }
-  return sq_smooth_scales_from_absmax(x_absmax, w_absmax, K, alpha, s, stream);
+  // no buffer for W's maxima: each workgroup finishes the maxima of its own
+  // columns over all of W and writes their factors (xa may be s: read, then written)
+  if (sq::launch_fill(xa, K, 0.0f, stream) != hipSuccess ||
+      sq::launch_col_absmax(X, x_t == SQ_BF16, T, K, xa, vx, cu_count(), stream) != hipSuccess)
+    return SQ_ERR_HIP;
+  return hip_status(sq::launch_smooth_scales_from_w(W, w_t == SQ_BF16, N, K, xa, alpha, s, vw, stream));
 }
 
 sq_status sq_quantize_weights(const void* W, sq_dtype w_t, int64_t N, int64_t K, const float* s,

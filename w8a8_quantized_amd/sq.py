@@ -89,11 +89,25 @@ def _dt(t, allowed=(torch.float32, torch.bfloat16)):
     return _DT[t.dtype]
 
 
+def _vec(t, n, name, dev, dtype=torch.float32, optional=False):
+    """Check a per-channel / per-token vector argument: n entries of `dtype` on
+    the device `dev` (None accepted when optional).  A short or wrongly typed
+    vector would be read past its end by the kernels, so it is refused here."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.numel() != n or t.dtype != dtype or t.device != torch.device(dev):
+        raise ValueError(f"{name} must be a {dtype} tensor of {n} entries on {dev} "
+                         f"(got {t.dtype}, {t.numel()} entries on {t.device})")
+    return t
+
+
 def _want(t, shape, dtype, dev):
     if t is None:
         return torch.empty(shape, dtype=dtype, device=dev)
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
-        raise ValueError(f"output must be {dtype} of shape {tuple(shape)}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != torch.device(dev):
+        raise ValueError(f"output must be {dtype} of shape {tuple(shape)} on {dev}")
     return t
 
 
@@ -109,25 +123,29 @@ def sq_col_absmax(A, amax=None, accumulate=False):
 def sq_smooth_scales_from_absmax(x_absmax, w_absmax, alpha, s=None):
     """s = max(xa,1e-8)^alpha / max(wa,1e-8)^(1-alpha)."""
     K = x_absmax.numel()
-    if w_absmax.numel() != K:
-        raise ValueError("x_absmax and w_absmax differ in length")
+    _vec(x_absmax, K, "x_absmax", x_absmax.device)
+    _vec(w_absmax, K, "w_absmax", x_absmax.device)
     s = _want(s, (K,), torch.float32, x_absmax.device)
     _check(_lib.sq_smooth_scales_from_absmax(_ptr(x_absmax), _ptr(w_absmax), K, float(alpha),
                                              _ptr(s), _stream(x_absmax.device)))
     return s
 
 
-def sq_smooth_scales(X, W, alpha, s=None, x_absmax=None, w_absmax=None):
+def sq_smooth_scales(X, W, alpha, s=None, x_absmax=None, w_absmax=None, maxima=(True, True)):
     """Smoothing factors from a calibration batch X [T, K] and weights W [N, K].
-    Returns (s, x_absmax, w_absmax)."""
+    Returns (s, x_absmax, w_absmax).  maxima = (False, ...) / (..., False)
+    passes NULL for that column-maxima output (the library then keeps no copy;
+    it is returned as None)."""
     T, K = X.shape
     N, K2 = W.shape
     if K != K2:
         raise ValueError("X and W differ in K")
     dev = X.device
+    if W.device != dev:
+        raise ValueError("X and W must be on the same device")
     s = _want(s, (K,), torch.float32, dev)
-    x_absmax = _want(x_absmax, (K,), torch.float32, dev)
-    w_absmax = _want(w_absmax, (K,), torch.float32, dev)
+    x_absmax = _want(x_absmax, (K,), torch.float32, dev) if maxima[0] else None
+    w_absmax = _want(w_absmax, (K,), torch.float32, dev) if maxima[1] else None
     _check(_lib.sq_smooth_scales(_ptr(X), _dt(X), T, _ptr(W), _dt(W), N, K, float(alpha), _ptr(s),
                                  _ptr(x_absmax), _ptr(w_absmax), _stream(dev)))
     return s, x_absmax, w_absmax
@@ -136,8 +154,7 @@ def sq_smooth_scales(X, W, alpha, s=None, x_absmax=None, w_absmax=None):
 def sq_quantize_weights(W, s=None, Wq=None, w_scale=None):
     """Per-output-channel int8 weights of W diag(s).  Returns (Wq, w_scale)."""
     N, K = W.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
+    _vec(s, K, "s", W.device, optional=True)
     Wq = _want(Wq, (N, K), torch.int8, W.device)
     w_scale = _want(w_scale, (N,), torch.float32, W.device)
     _check(_lib.sq_quantize_weights(_ptr(W), _dt(W), N, K, _ptr(s), _ptr(Wq), _ptr(w_scale),
@@ -148,8 +165,7 @@ def sq_quantize_weights(W, s=None, Wq=None, w_scale=None):
 def sq_quant_act(X, s=None, Xq=None, x_scale=None):
     """Dynamic per-token int8 codes of X diag(s)^-1.  Returns (Xq, x_scale)."""
     T, K = X.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
+    _vec(s, K, "s", X.device, optional=True)
     Xq = _want(Xq, (T, K), torch.int8, X.device)
     x_scale = _want(x_scale, (T,), torch.float32, X.device)
     _check(_lib.sq_quant_act(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(Xq), _ptr(x_scale),
@@ -160,8 +176,7 @@ def sq_quant_act(X, s=None, Xq=None, x_scale=None):
 def sq_act_absmax(X, s=None, amax=None, accumulate=False):
     """Range of X diag(s)^-1 over the whole tensor, as a device float [1]."""
     T, K = X.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
+    _vec(s, K, "s", X.device, optional=True)
     amax = _want(amax, (1,), torch.float32, X.device)
     _check(_lib.sq_act_absmax(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(amax), int(bool(accumulate)),
                               _stream(X.device)))
@@ -172,10 +187,8 @@ def sq_quant_act_static(X, s, clip, Xq=None, x_scale=None):
     """Per-tensor int8 codes of X diag(s)^-1 against the range clip (device float
     [1]).  Returns (Xq, x_scale), every x_scale entry the tensor's scale."""
     T, K = X.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
-    if clip is None or clip.numel() != 1 or clip.dtype != torch.float32:
-        raise ValueError("clip must be a float32 tensor of one element")
+    _vec(s, K, "s", X.device, optional=True)
+    _vec(clip, 1, "clip", X.device)
     Xq = _want(Xq, (T, K), torch.int8, X.device)
     x_scale = _want(x_scale, (T,), torch.float32, X.device)
     _check(_lib.sq_quant_act_static(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(clip), _ptr(Xq),
@@ -186,8 +199,7 @@ def sq_quant_act_static(X, s, clip, Xq=None, x_scale=None):
 def sq_quant_act_per_tensor(X, s=None, amax=None, Xq=None, x_scale=None):
     """Dynamic per-tensor int8 codes of X diag(s)^-1.  Returns (Xq, x_scale, amax)."""
     T, K = X.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
+    _vec(s, K, "s", X.device, optional=True)
     amax = _want(amax, (1,), torch.float32, X.device)
     Xq = _want(Xq, (T, K), torch.int8, X.device)
     x_scale = _want(x_scale, (T,), torch.float32, X.device)
@@ -198,8 +210,8 @@ def sq_quant_act_per_tensor(X, s=None, amax=None, Xq=None, x_scale=None):
 
 def sq_fold_norm_gain(v, s, out=None):
     """v / s per channel (a norm's gain or bias with the smoothing folded in)."""
-    if v.numel() != s.numel():
-        raise ValueError("v and s must have the same length")
+    _vec(s, v.numel(), "s", v.device)
+    _vec(v, v.numel(), "v", v.device)
     out = _want(out, (v.numel(),), torch.float32, v.device)
     _check(_lib.sq_fold_norm_gain(_ptr(v), _ptr(s), v.numel(), _ptr(out), _stream(v.device)))
     return out
@@ -212,8 +224,8 @@ def sq_norm_quant_act(X, kind, gain, bias=None, eps=1e-6, Xq=None, x_scale=None,
     T, K = X.shape
     if kind not in _NORM:
         raise ValueError(f"kind must be one of {tuple(_NORM)}")
-    if gain.numel() != K or (bias is not None and bias.numel() != K):
-        raise ValueError("gain and bias must have K entries")
+    _vec(gain, K, "gain", X.device)
+    _vec(bias, K, "bias", X.device, optional=True)
     Xq = _want(Xq, (T, K), torch.int8, X.device)
     x_scale = _want(x_scale, (T,), torch.float32, X.device)
     mean = _want(mean, (T,), torch.float32, X.device)
@@ -227,6 +239,7 @@ def sq_norm_quant_act(X, kind, gain, bias=None, eps=1e-6, Xq=None, x_scale=None,
 def sq_decomp_select(absmax, n_o, idx=None, mask=None):
     """The n_o channels of largest absmax (ascending) and the 0/1 column mask."""
     K = absmax.numel()
+    _vec(absmax, K, "absmax", absmax.device)
     idx = _want(idx, (n_o,), torch.int32, absmax.device)
     mask = _want(mask, (K,), torch.float32, absmax.device)
     _check(_lib.sq_decomp_select(_ptr(absmax), K, int(n_o), _ptr(idx) if n_o else None, _ptr(mask),
@@ -238,6 +251,8 @@ def sq_decomp_prepare_weights(W, mask, idx, Wq=None, w_scale=None, W_out=None):
     """Bulk int8 weights (outlier columns zeroed), w_scale, W_out [n_o, N]."""
     N, K = W.shape
     n_o = idx.numel()
+    _vec(mask, K, "mask", W.device)
+    _vec(idx, n_o, "idx", W.device, dtype=torch.int32)
     Wq = _want(Wq, (N, K), torch.int8, W.device)
     w_scale = _want(w_scale, (N,), torch.float32, W.device)
     W_out = _want(W_out, (n_o, N), torch.float32, W.device)
@@ -251,6 +266,8 @@ def sq_decomp_quant_act(X, mask, idx, Xq=None, x_scale=None, X_out=None):
     """Bulk per-token int8 codes (outlier columns zeroed), x_scale, X_out [n_o, T]."""
     T, K = X.shape
     n_o = idx.numel()
+    _vec(mask, K, "mask", X.device)
+    _vec(idx, n_o, "idx", X.device, dtype=torch.int32)
     Xq = _want(Xq, (T, K), torch.int8, X.device)
     x_scale = _want(x_scale, (T,), torch.float32, X.device)
     X_out = _want(X_out, (n_o, T), torch.float32, X.device)
@@ -267,6 +284,12 @@ def sq_decomp_gemm(Xq, x_scale, Wq, w_scale, X_out, W_out, out_dtype=torch.bfloa
     n_o = X_out.shape[0]
     if K != K2 or tuple(W_out.shape) != (n_o, N) or X_out.shape[1] != T:
         raise ValueError("shapes: Xq [T, K], Wq [N, K], X_out [n_o, T], W_out [n_o, N]")
+    if Xq.dtype != torch.int8 or Wq.dtype != torch.int8 or Wq.device != Xq.device:
+        raise ValueError("Xq and Wq must be int8 on the same device")
+    _vec(x_scale, T, "x_scale", Xq.device)
+    _vec(w_scale, N, "w_scale", Xq.device)
+    _vec(X_out, n_o * T, "X_out", Xq.device)
+    _vec(W_out, n_o * N, "W_out", Xq.device)
     yt = _DT.get(out_dtype)
     if yt is None or out_dtype == torch.int32:
         raise ValueError(f"out_dtype {out_dtype} not accepted")
@@ -280,8 +303,7 @@ def sq_decomp_gemm(Xq, x_scale, Wq, w_scale, X_out, W_out, out_dtype=torch.bfloa
 def sq_quantize_weights_fp8(W, s=None, Wq=None, w_scale=None):
     """Per-output-channel FP8 E4M3 codes (uint8) of W diag(s).  Returns (Wq, w_scale)."""
     N, K = W.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
+    _vec(s, K, "s", W.device, optional=True)
     Wq = _want(Wq, (N, K), torch.uint8, W.device)
     w_scale = _want(w_scale, (N,), torch.float32, W.device)
     _check(_lib.sq_quantize_weights_fp8(_ptr(W), _dt(W), N, K, _ptr(s), _ptr(Wq), _ptr(w_scale),
@@ -292,8 +314,7 @@ def sq_quantize_weights_fp8(W, s=None, Wq=None, w_scale=None):
 def sq_quant_act_fp8(X, s=None, Xq=None, x_scale=None):
     """Per-token FP8 E4M3 codes (uint8) of X diag(s)^-1.  Returns (Xq, x_scale)."""
     T, K = X.shape
-    if s is not None and s.numel() != K:
-        raise ValueError("s must have K entries")
+    _vec(s, K, "s", X.device, optional=True)
     Xq = _want(Xq, (T, K), torch.uint8, X.device)
     x_scale = _want(x_scale, (T,), torch.float32, X.device)
     _check(_lib.sq_quant_act_fp8(_ptr(X), _dt(X), T, K, _ptr(s), _ptr(Xq), _ptr(x_scale),
@@ -305,8 +326,10 @@ def sq_fp8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
     """Y = dequant(e4m3(Xq) @ e4m3(Wq)^T) on the FP8 matrix cores."""
     T, K = Xq.shape
     N, K2 = Wq.shape
-    if K != K2 or Xq.dtype != torch.uint8 or Wq.dtype != torch.uint8:
-        raise ValueError("Xq [T, K] and Wq [N, K] must be uint8 E4M3 codes with the same K")
+    if K != K2 or Xq.dtype != torch.uint8 or Wq.dtype != torch.uint8 or Wq.device != Xq.device:
+        raise ValueError("Xq [T, K] and Wq [N, K] must be uint8 E4M3 codes with the same K, on one device")
+    _vec(x_scale, T, "x_scale", Xq.device)
+    _vec(w_scale, N, "w_scale", Xq.device)
     yt = _DT.get(out_dtype)
     if yt is None or out_dtype == torch.int32:
         raise ValueError(f"out_dtype {out_dtype} not accepted")
@@ -320,11 +343,14 @@ def sq_w8a8_gemm(Xq, x_scale, Wq, w_scale, out_dtype=torch.bfloat16, Y=None):
     """Y = dequant(Xq @ Wq^T); out_dtype torch.int32 returns the raw accumulators."""
     T, K = Xq.shape
     N, K2 = Wq.shape
-    if K != K2 or Xq.dtype != torch.int8 or Wq.dtype != torch.int8:
-        raise ValueError("Xq [T, K] and Wq [N, K] must be int8 with the same K")
+    if K != K2 or Xq.dtype != torch.int8 or Wq.dtype != torch.int8 or Wq.device != Xq.device:
+        raise ValueError("Xq [T, K] and Wq [N, K] must be int8 with the same K, on one device")
     yt = _DT.get(out_dtype)
     if yt is None:
         raise ValueError(f"out_dtype {out_dtype} not accepted")
+    # the raw int32 accumulators need no scales (they may be None)
+    _vec(x_scale, T, "x_scale", Xq.device, optional=out_dtype == torch.int32)
+    _vec(w_scale, N, "w_scale", Xq.device, optional=out_dtype == torch.int32)
     Y = _want(Y, (T, N), out_dtype, Xq.device)
     _check(_lib.sq_w8a8_gemm(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), T, N, K, _ptr(Y),
                              yt, _stream(Xq.device)))
@@ -339,8 +365,10 @@ def sq_w8a8_linear(X, s, Wq, w_scale, out_dtype=torch.bfloat16, Y=None, workspac
     """Run-time layer: per-token quantisation of X diag(s)^-1, then the W8A8 GEMM."""
     T, K = X.shape
     N, K2 = Wq.shape
-    if K != K2:
-        raise ValueError("X and Wq differ in K")
+    if K != K2 or Wq.dtype != torch.int8 or Wq.device != X.device:
+        raise ValueError("Wq must be int8 [N, K] on X's device")
+    _vec(s, K, "s", X.device, optional=True)
+    _vec(w_scale, N, "w_scale", X.device)
     yt = _DT.get(out_dtype)
     if yt is None or out_dtype == torch.int32:
         raise ValueError(f"out_dtype {out_dtype} not accepted")
