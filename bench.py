@@ -12,7 +12,7 @@ through libsq.so on the current HIP stream:
 `value` is 2*T*N*K / (time per step) in TOPS, with inputs resident in HBM.  In
 the timed region one pair of HIP events per step, on the same stream, brackets
 the GEMM (the dominant kernel) for the roofline figure; the per-call breakdown
-is measured afterwards with batched back-to-back launches.  Default workload: heavy-outlier prefill,
+is measured before the warm-up, with batched back-to-back launches.  Default workload: heavy-outlier prefill,
 X bf16 [8192 x 8192] (30% outlier channels), W [8192 x 8192], alpha 0.75, bf16 out.
 
 Also printed in the same JSON line: the GEMM's roofline fraction against the
@@ -83,11 +83,22 @@ def _omp_threads():
         return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
-def cpu_baseline(w, target_s=20.0):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, target_s=20.0, runs=3):
     """The oracle as it stands, on a prefix of the workload's tokens: statistics,
     smoothing factors and weight quantisation in full, then quantisation, integer
     GEMM, epilogue and bf16 rounding for `tokens` tokens.  Throughput in TOPS of
-    the sample's 2*tokens*N*K over the wall time of all of it."""
+    the sample's 2*tokens*N*K over the wall time of all of it; the median of
+    `runs` runs, each sized for about target_s / runs seconds."""
     import oracle as O
     O.build()
 
@@ -109,15 +120,20 @@ def cpu_baseline(w, target_s=20.0):
     t0 = time.perf_counter()
     runtime(s, Wq, ws, probe)
     per_token = (time.perf_counter() - t0) / probe
-    tokens = int(max(1, min(w.T, target_s / max(per_token, 1e-6))))
-    t0 = time.perf_counter()
-    s, Wq, ws = offline()
-    runtime(s, Wq, ws, tokens)
-    dt = time.perf_counter() - t0
-    return {"value": 2.0 * tokens * w.N * w.K / dt / 1e12, "unit": "TOPS", "cores": _omp_threads(),
-            "kind": "oracle",
+    tokens = int(max(1, min(w.T, target_s / runs / max(per_token, 1e-6))))
+    rates, walls = [], []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        s, Wq, ws = offline()
+        runtime(s, Wq, ws, tokens)
+        dt = time.perf_counter() - t0
+        walls.append(dt)
+        rates.append(2.0 * tokens * w.N * w.K / dt / 1e12)
+    return {"value": float(np.median(rates)), "unit": "TOPS", "cores": _omp_threads(),
+            "cpu_model": _cpu_model(), "runs": runs, "kind": "oracle",
             "sample": f"first {tokens} of {w.T} tokens; column maxima, smoothing factors and weight "
-                      f"quantisation over the full tensors; {dt:.1f} s wall"}
+                      f"quantisation over the full tensors; median of {runs} runs of "
+                      f"{', '.join(f'{d:.1f}' for d in walls)} s wall"}
 
 
 def decode_measure(sq, torch, reps=30):
@@ -315,6 +331,61 @@ def main():
         sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=ydt, Y=Y)
         if ev: ev[1].record()
 
+    # Per-call figures first, then the timed steps: the GPU runs at a lower clock
+    # for its first ~20 ms of load, and measured after that settling (rather than
+    # right after the warm-up steps) the step and its GEMM reflect the sustained
+    # rate.  Decode-shaped and decomposition figures (their own workloads) come
+    # first, then this workload's entry points, each launched `reps` times back
+    # to back between two events, cycling through 3 copies of its large input so
+    # that every launch reads from HBM rather than from the 256 MB Infinity
+    # Cache.  The int8 GEMM of this workload is not among them: its per-launch
+    # time comes from the timed region itself.
+    extra = {}
+    if not args.no_decode:
+        extra["decode_gemm"] = decode_measure(sq, torch)
+        extra["decomposition"] = decomp_measure(sq, torch)
+        torch.cuda.empty_cache()
+
+    def batched(fn, copies, reps=12):
+        fn(copies[0])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(copies[i % len(copies)])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    step()
+    Wc = [W, W.clone(), W.clone()]
+    Xc = [X, X.clone(), X.clone()]
+    # FP8 E4M3 variant of the same layer: quantisers and the FP8 matrix-core GEMM
+    Wq8, ws8 = sq.sq_quantize_weights_fp8(W, s)
+    Xq8, xs8 = sq.sq_quant_act_fp8(X, s)
+    t_q8 = batched(lambda x_: sq.sq_quant_act_fp8(x_, s, Xq=Xq8, x_scale=xs8), Xc)
+    t_g8 = batched(lambda _: sq.sq_fp8_gemm(Xq8, xs8, Wq8, ws8, out_dtype=ydt, Y=Y), [None])
+    del Wq8, Xq8
+    # per-tensor activation scales: the range reduction alone, the static-range
+    # quantiser (range from the first 512 tokens, as a calibration would give),
+    # and the dynamic per-tensor quantiser (reduction + quantiser)
+    amax_buf = torch.empty(1, device=dev)
+    clip_buf = sq.sq_act_absmax(X[:512], s)
+    t_tabs = batched(lambda x_: sq.sq_act_absmax(x_, s, amax=amax_buf), Xc)
+    t_qstat = batched(lambda x_: sq.sq_quant_act_static(x_, s, clip_buf, Xq=Xq, x_scale=xs), Xc)
+    t_qpt = batched(lambda x_: sq.sq_quant_act_per_tensor(x_, s, amax=amax_buf, Xq=Xq, x_scale=xs), Xc)
+    # the producer in front of the layer: RMSNorm (gain folded with s) + per-token int8
+    gen = torch.Generator(device=dev).manual_seed(7)
+    gain = 1.0 + 0.2 * torch.randn(K, device=dev, generator=gen)
+    gfold = sq.sq_fold_norm_gain(gain, s)
+    m_buf, r_buf = torch.empty(T, device=dev), torch.empty(T, device=dev)
+    t_norm = batched(lambda x_: sq.sq_norm_quant_act(x_, "rms", gfold, Xq=Xq, x_scale=xs, mean=m_buf,
+                                                     rstd=r_buf), Xc)
+    t_smooth = batched(lambda w_: sq.sq_smooth_scales(Xs, w_, w.alpha, s=s, x_absmax=xa, w_absmax=wa), Wc)
+    t_wq = batched(lambda w_: sq.sq_quantize_weights(w_, s, Wq=Wq, w_scale=ws), Wc)
+    t_quant = batched(lambda x_: sq.sq_quant_act(x_, s, Xq=Xq, x_scale=xs), Xc)
+    del Wc, Xc
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -343,48 +414,6 @@ def main():
     launch_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
     t_gemm = float(np.mean(launch_ms))
 
-    # per-call breakdown outside the timed region: each entry point launched
-    # `reps` times back to back between two events (launch gaps amortised),
-    # cycling through 3 copies of its large input so that every launch reads
-    # from HBM rather than from the 256 MB Infinity Cache
-    def batched(fn, copies, reps=12):
-        fn(copies[0])
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(reps):
-            fn(copies[i % len(copies)])
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    Wc = [W, W.clone(), W.clone()]
-    Xc = [X, X.clone(), X.clone()]
-    t_smooth = batched(lambda w_: sq.sq_smooth_scales(Xs, w_, w.alpha, s=s, x_absmax=xa, w_absmax=wa), Wc)
-    t_wq = batched(lambda w_: sq.sq_quantize_weights(w_, s, Wq=Wq, w_scale=ws), Wc)
-    t_quant = batched(lambda x_: sq.sq_quant_act(x_, s, Xq=Xq, x_scale=xs), Xc)
-    t_gemm_b = batched(lambda _: sq.sq_w8a8_gemm(Xq, xs, Wq, ws, out_dtype=ydt, Y=Y), [None])
-    # per-tensor activation scales: the range reduction alone, the static-range
-    # quantiser (range from the first 512 tokens, as a calibration would give),
-    # and the dynamic per-tensor quantiser (reduction + quantiser)
-    amax_buf = torch.empty(1, device=dev)
-    clip_buf = sq.sq_act_absmax(X[:512], s)
-    t_tabs = batched(lambda x_: sq.sq_act_absmax(x_, s, amax=amax_buf), Xc)
-    t_qstat = batched(lambda x_: sq.sq_quant_act_static(x_, s, clip_buf, Xq=Xq, x_scale=xs), Xc)
-    t_qpt = batched(lambda x_: sq.sq_quant_act_per_tensor(x_, s, amax=amax_buf, Xq=Xq, x_scale=xs), Xc)
-    # the producer in front of the layer: RMSNorm (gain folded with s) + per-token int8
-    gen = torch.Generator(device=dev).manual_seed(7)
-    gain = 1.0 + 0.2 * torch.randn(K, device=dev, generator=gen)
-    gfold = sq.sq_fold_norm_gain(gain, s)
-    m_buf, r_buf = torch.empty(T, device=dev), torch.empty(T, device=dev)
-    t_norm = batched(lambda x_: sq.sq_norm_quant_act(x_, "rms", gfold, Xq=Xq, x_scale=xs, mean=m_buf,
-                                                     rstd=r_buf), Xc)
-    # FP8 E4M3 variant of the same layer: quantisers and the FP8 matrix-core GEMM
-    Wq8, ws8 = sq.sq_quantize_weights_fp8(W, s)
-    Xq8, xs8 = sq.sq_quant_act_fp8(X, s)
-    t_q8 = batched(lambda x_: sq.sq_quant_act_fp8(x_, s, Xq=Xq8, x_scale=xs8), Xc)
-    t_g8 = batched(lambda _: sq.sq_fp8_gemm(Xq8, xs8, Wq8, ws8, out_dtype=ydt, Y=Y), [None])
-    del Wc, Xc, Wq8, Xq8
     ops = 2.0 * T * N * K
     ob = 2 if ydt == torch.bfloat16 else 4
     ib = 2 if xdt == torch.bfloat16 else 4
@@ -410,7 +439,7 @@ def main():
                      "per_launch_ops": ops, "avg_launch_ms": t_gemm, "timed_launches": len(timed),
                      "launch_ms_p10_p50_p90": [float(np.percentile(launch_ms, q)) for q in (10, 50, 90)]},
         "breakdown_ms_batched": {"smooth_scales": t_smooth, "quantize_weights": t_wq,
-                                 "quant_act": t_quant, "w8a8_gemm": t_gemm_b},
+                                 "quant_act": t_quant},
         "linear_tops": ops / ((t_quant + t_gemm) * 1e-3) / 1e12,
         "quant_act": {"GB/s": qbytes / (t_quant * 1e-3) / 1e9,
                       "frac_hbm": qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": qbytes},
@@ -426,12 +455,10 @@ def main():
                 "gemm_frac_fp8_peak": ops / (t_g8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
                 "linear_TFLOP/s": ops / ((t_q8 + t_g8) * 1e-3) / 1e12},
     }
-    if not args.no_decode:
+    out.update(extra)
+    if not args.no_cpu:
         del X, Xs, W, Wq, Xq, Y
         torch.cuda.empty_cache()
-        out["decode_gemm"] = decode_measure(sq, torch)
-        out["decomposition"] = decomp_measure(sq, torch)
-    if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 
