@@ -61,7 +61,8 @@ typedef enum sq_status {
     SQ_ERR_DTYPE = 4,      /* dtype not accepted for that argument               */
     SQ_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required            */
     SQ_ERR_HIP = 6,        /* the HIP runtime rejected a launch                  */
-    SQ_ERR_ARG = 7         /* an argument value is not accepted (see the call)   */
+    SQ_ERR_ARG = 7,        /* an argument value is not accepted (see the call)   */
+    SQ_ERR_SCRATCH = 8     /* more scratch than the no-allocation call holds     */
 } sq_status;
 
 typedef enum sq_dtype {
@@ -379,6 +380,31 @@ sq_status sq_w8a8_linear(const void *X, sq_dtype x_t, const float *s,
                          const int8_t *Wq, const float *w_scale,
                          int64_t T, int64_t N, int64_t K, void *Y, sq_dtype y_t,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the library's fixed per-GPU scratch used by sq_w8a8_linear_noalloc. */
+#define SQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * sq_w8a8_linear with the workspace taken from a fixed array of
+ * SQ_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on, from
+ * the first such call until the process ends.  The call allocates nothing; the
+ * caller passes inputs and outputs as for sq_w8a8_linear, and the results are
+ * bit for bit those of sq_w8a8_linear.
+ *   SQ_ERR_SCRATCH  sq_w8a8_linear_workspace_size(T, K) exceeds
+ *                   SQ_NOALLOC_SCRATCH_BYTES (T * K up to ~32 M int8 codes);
+ *                   nothing is launched
+ *   SQ_ERR_HIP      also when the scratch's address cannot be obtained
+ * Every call on one GPU uses the same scratch: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be ordered by the caller.
+ * Nothing in the scratch needs to start at zero (each call writes the codes
+ * and scales before its GEMM reads them).
+ */
+sq_status sq_w8a8_linear_noalloc(const void *X, sq_dtype x_t, const float *s,
+                                 const int8_t *Wq, const float *w_scale,
+                                 int64_t T, int64_t N, int64_t K, void *Y, sq_dtype y_t,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,7 @@ LIB = os.path.join(ROOT, "w8a8_quantized_amd", "libsq.so")
 HEADER = os.path.join(ROOT, "include", "sq.h")
 
 (SQ_OK, SQ_ERR_NULL, SQ_ERR_SHAPE, SQ_ERR_ALPHA, SQ_ERR_DTYPE, SQ_ERR_WORKSPACE, SQ_ERR_HIP,
- SQ_ERR_ARG) = range(8)
+ SQ_ERR_ARG, SQ_ERR_SCRATCH) = range(9)
 F32, BF16, I32 = 0, 1, 2
 
 
@@ -67,7 +67,7 @@ def test_binding_names_match_header():
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.sq_status_string(code).decode()
         assert s.startswith("SQ_"), s
     assert b"unknown" in lib.sq_status_string(99)
@@ -189,3 +189,20 @@ def test_decomp_arguments(lib):
     assert lib.sq_decomp_gemm(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 4, 16, 2, FAKE, F32, None) == SQ_ERR_NULL
     assert lib.sq_decomp_gemm(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004), FAKE, 4, 4, 16, 2, FAKE, F32,
                               None) == SQ_ERR_ARG
+
+
+def test_noalloc_arguments(lib):
+    """The no-allocation layer call validates on the host like sq_w8a8_linear
+    and refuses problems whose codes and scales exceed its fixed scratch
+    (32 MiB) before any launch."""
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.sq_w8a8_linear_noalloc.argtypes = [P, I, P, P, P, I64, I64, I64, P, I, P]
+    f = lib.sq_w8a8_linear_noalloc
+    assert f(None, BF16, None, FAKE, FAKE, 4, 4, 16, FAKE, BF16, None) == SQ_ERR_NULL
+    assert f(FAKE, BF16, None, FAKE, None, 4, 4, 16, FAKE, BF16, None) == SQ_ERR_NULL
+    assert f(FAKE, BF16, None, FAKE, FAKE, 4, 4, 16, FAKE, I32, None) == SQ_ERR_DTYPE
+    assert f(FAKE, BF16, None, FAKE, FAKE, 0, 4, 16, FAKE, BF16, None) == SQ_ERR_SHAPE
+    # 8192 x 8192 codes (64 MiB) and one token past 32 MiB of codes
+    assert f(FAKE, BF16, None, FAKE, FAKE, 8192, 8192, 8192, FAKE, BF16, None) == SQ_ERR_SCRATCH
+    assert f(FAKE, BF16, None, FAKE, FAKE, 4097, 4, 8192, FAKE, BF16, None) == SQ_ERR_SCRATCH
+    assert b"SQ_ERR_SCRATCH" in lib.sq_status_string(SQ_ERR_SCRATCH)

@@ -11,4 +11,5 @@ from .sq import (SQ_BF16, SQ_F32, SQ_I32, SQ_MAX_K, EXPORTED, LIB_PATH,  # noqa:
                  sq_act_absmax, sq_col_absmax, sq_quant_act, sq_quant_act_per_tensor,
                  sq_quant_act_static, sq_quantize_weights, sq_smooth_scales,
                  sq_smooth_scales_from_absmax, sq_status_string, sq_w8a8_gemm, sq_w8a8_linear,
-                 sq_w8a8_linear_workspace_size)
+                 sq_w8a8_linear_workspace_size, sq_w8a8_linear_noalloc,
+                 SQ_NOALLOC_SCRATCH_BYTES)

@@ -2,9 +2,16 @@
 // The semantics of each entry point are documented in include/sq.h.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/sq.h"
 #include "kernels.h"
+
+// Fixed scratch of the no-allocation layer call, one copy per GPU (the
+// workspace of sq_w8a8_linear: int8 codes, then the per-token scales).  In host
+// code `scratch` is only a handle to the symbol; its device address on each GPU
+// comes from hipGetSymbolAddress and is what kernels are given.
+static __device__ __align__(256) unsigned char scratch[SQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -90,6 +97,27 @@ sq_status run_quant_static(const void* X, sq_dtype x_t, int64_t T, int64_t K, co
                                           xs, vec, cu_count(), st));
 }
 
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's scratch (looked up once per device), or
+// nullptr if it cannot be obtained.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,6 +132,9 @@ const char* sq_status_string(sq_status status) {
     case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
     case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime rejected a launch";
     case SQ_ERR_ARG: return "SQ_ERR_ARG: an argument value is not accepted";
+    case SQ_ERR_SCRATCH:
+      return "SQ_ERR_SCRATCH: the problem needs more than the no-allocation call's fixed scratch "
+             "(SQ_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown sq_status";
 }
@@ -323,6 +354,24 @@ sq_status sq_w8a8_linear(const void* X, sq_dtype x_t, const float* s, const int8
     return SQ_ERR_WORKSPACE;
   int8_t* Xq = static_cast<int8_t*>(workspace);
   float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)T * (size_t)K));
+  sq_status r = run_quant_act(X, x_t, T, K, s, Xq, xs, stream);
+  if (r != SQ_OK) return r;
+  return run_gemm(Xq, xs, Wq, w_scale, T, N, K, Y, y_t, stream);
+}
+
+sq_status sq_w8a8_linear_noalloc(const void* X, sq_dtype x_t, const float* s, const int8_t* Wq,
+                                 const float* w_scale, int64_t T, int64_t N, int64_t K, void* Y, sq_dtype y_t,
+                                 hipStream_t stream) {
+  if (!X || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
+  if (!in_dtype(x_t) || !in_dtype(y_t)) return SQ_ERR_DTYPE;
+  if (T < 1 || N < 1 || K < 1 || K > SQ_MAX_K) return SQ_ERR_SHAPE;
+  if ((uint64_t)T * (uint64_t)K > SQ_NOALLOC_SCRATCH_BYTES ||
+      sq_w8a8_linear_workspace_size(T, K) > SQ_NOALLOC_SCRATCH_BYTES)
+    return SQ_ERR_SCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return SQ_ERR_HIP;
+  int8_t* Xq = static_cast<int8_t*>(ws);
+  float* xs = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)T * (size_t)K));
   sq_status r = run_quant_act(X, x_t, T, K, s, Xq, xs, stream);
   if (r != SQ_OK) return r;
   return run_gemm(Xq, xs, Wq, w_scale, T, N, K, Y, y_t, stream);

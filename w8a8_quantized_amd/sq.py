@@ -21,6 +21,7 @@ SQ_F32, SQ_BF16, SQ_I32 = 0, 1, 2
 SQ_NORM_RMS, SQ_NORM_LAYER = 0, 1
 _NORM = {"rms": SQ_NORM_RMS, "layer": SQ_NORM_LAYER}
 SQ_MAX_K = 133144
+SQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 _DT = {torch.float32: SQ_F32, torch.bfloat16: SQ_BF16, torch.int32: SQ_I32}
 
 if not os.path.exists(LIB_PATH):
@@ -51,6 +52,7 @@ _SIGS = {
     "sq_w8a8_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "sq_w8a8_linear_workspace_size": ([_I64, _I64], _SZ),
     "sq_w8a8_linear": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P], _I),
+    "sq_w8a8_linear_noalloc": ([_P, _I, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -379,4 +381,25 @@ def sq_w8a8_linear(X, s, Wq, w_scale, out_dtype=torch.bfloat16, Y=None, workspac
     _check(_lib.sq_w8a8_linear(_ptr(X), _dt(X), _ptr(s), _ptr(Wq), _ptr(w_scale), T, N, K, _ptr(Y),
                                yt, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(X.device)))
+    return Y
+
+
+def sq_w8a8_linear_noalloc(X, s, Wq, w_scale, Y, out_dtype=torch.bfloat16):
+    """sq_w8a8_linear with the workspace in the library's fixed per-GPU scratch
+    (for callers that cannot allocate): Y must be passed in; calls that overlap
+    on one GPU race."""
+    T, K = X.shape
+    N, K2 = Wq.shape
+    if K != K2 or Wq.dtype != torch.int8 or Wq.device != X.device:
+        raise ValueError("Wq must be int8 [N, K] on X's device")
+    _vec(s, K, "s", X.device, optional=True)
+    _vec(w_scale, N, "w_scale", X.device)
+    yt = _DT.get(out_dtype)
+    if yt is None or out_dtype == torch.int32:
+        raise ValueError(f"out_dtype {out_dtype} not accepted")
+    if Y is None:
+        raise ValueError("Y must be passed in (this call allocates nothing)")
+    Y = _want(Y, (T, N), out_dtype, X.device)
+    _check(_lib.sq_w8a8_linear_noalloc(_ptr(X), _dt(X), _ptr(s), _ptr(Wq), _ptr(w_scale), T, N, K, _ptr(Y),
+                                       yt, _stream(X.device)))
     return Y
