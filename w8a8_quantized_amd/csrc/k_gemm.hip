@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "slices.h"
 
 namespace sq {
 
@@ -705,9 +706,8 @@ template <int BN, int BT, int BK, int WN, int WT, int ST, bool F8 = false, bool 
 static hipError_t gemm_cfg(const GemmArgs& a, hipStream_t st, int ncu = 0) {
   // Split so that every operand slice handed to one launch spans < 2^31 bytes
   // (32-bit buffer offsets), counting one tile of overhang past the edge.
-  const int64_t lim = (int64_t)1 << 31;
-  const int64_t n_chunk = ((lim / a.K - BN) / BN) * BN;
-  const int64_t t_chunk = ((lim / a.K - BT) / BT) * BT;
+  const int64_t n_chunk = rows_per_slice(a.K, BN);
+  const int64_t t_chunk = rows_per_slice(a.K, BT);
   const size_t osz = a.out == kOutBF16 ? 2 : 4;
   for (int64_t tb = 0; tb < a.T; tb += t_chunk) {
     const int T = (int)(a.T - tb < t_chunk ? a.T - tb : t_chunk);

@@ -28,6 +28,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "slices.h"
 
 namespace sq {
 
@@ -401,8 +402,7 @@ constexpr size_t kGemvOutlierLds = 64 * 1024;
 template <int NB, int TB, int KW, bool F8>
 static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
   // split N so that one launch's weight slice spans < 2^31 bytes (32-bit offsets)
-  const int64_t lim = (int64_t)1 << 31;
-  const int64_t n_chunk = ((lim / a.K - 16 * NB) / (16 * NB)) * (16 * NB);
+  const int64_t n_chunk = rows_per_slice(a.K, 16 * NB);
   const size_t osz = a.out == kOutBF16 ? 2 : 4;
   for (int64_t nb = 0; nb < a.N; nb += n_chunk) {
     const int N = (int)(a.N - nb < n_chunk ? a.N - nb : n_chunk);
