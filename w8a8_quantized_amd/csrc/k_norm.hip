@@ -175,18 +175,27 @@ __global__ __launch_bounds__(256) void norm_quant_rows_kernel(
     }
   };
 
+  // Unconditional prefetch (past the last row it re-reads row R - 1, an L2
+  // hit), held ahead of the row's arithmetic by a scheduling barrier: under a
+  // branch the compiler waited for every outstanding load, the prefetch
+  // included, before each row (RMSNorm 8192 x 8192 bf16: 37.4 against 39.4 us,
+  // bit-identical).
   Row8<T> ba[CPT], bb[CPT];
   const int64_t G = gridDim.x;
   int64_t r = blockIdx.x;
-  if (r < R) load(ba, r);
-  while (r < R) {
-    if (r + G < R) load(bb, r + G);
+  if (r >= R) return;
+  load(ba, r);
+  while (true) {
+    load(bb, r + G < R ? r + G : R - 1);
+    __builtin_amdgcn_sched_barrier(0);
     process(ba, r);
     r += G;
-    if (r >= R) break;
-    if (r + G < R) load(ba, r + G);
+    if (r >= R) return;
+    load(ba, r + G < R ? r + G : R - 1);
+    __builtin_amdgcn_sched_barrier(0);
     process(bb, r);
     r += G;
+    if (r >= R) return;
   }
 }
 

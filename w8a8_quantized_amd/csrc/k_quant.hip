@@ -192,19 +192,28 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ A
   };
 
   // rows r, r + G, r + 2G, ... alternating between two register buffers; the
-  // next row's loads are in flight while the current one is processed
+  // next row's loads are in flight while the current one is processed.  The
+  // prefetch is unconditional (past the last row it re-reads row R - 1, an L2
+  // hit) and held ahead of the row's arithmetic by a scheduling barrier: a
+  // prefetch under a branch made the compiler wait for every outstanding load
+  // (the prefetch included) before each row, and the weight quantiser ran 3%
+  // slower that way (8192 x 8192 fp32, bit-identical).
   Raw8<T> ba[CPT], bb[CPT];
   const int64_t G = gridDim.x;
   int64_t r = blockIdx.x;
-  if (r < R) load(ba, r);
-  while (r < R) {
-    if (r + G < R) load(bb, r + G);
+  if (r >= R) return;
+  load(ba, r);
+  while (true) {
+    load(bb, r + G < R ? r + G : R - 1);
+    __builtin_amdgcn_sched_barrier(0);
     process(ba, r);
     r += G;
-    if (r >= R) break;
-    if (r + G < R) load(ba, r + G);
+    if (r >= R) return;
+    load(ba, r + G < R ? r + G : R - 1);
+    __builtin_amdgcn_sched_barrier(0);
     process(bb, r);
     r += G;
+    if (r >= R) return;
   }
 }
 
