@@ -239,9 +239,10 @@ def decomp_measure(sq, torch):
 def configs_report(sq, torch):
     """Per-configuration figures (one JSON object per line, not the contract
     line): the run-time layer (sq_quant_act + sq_w8a8_gemm) on each named
-    workload with its own smoothing factors, timed as back-to-back calls.  The
-    large inputs are rotated over three copies when they exceed the Infinity
-    Cache."""
+    workload with its own smoothing factors, timed as 7 batches of 20
+    back-to-back calls (median and 10th / 90th percentile of the batch means).
+    The large inputs are rotated over three copies when they exceed the
+    Infinity Cache."""
     import workloads as WL
     dev = torch.device("cuda")
     for name in WL.WORKLOADS:
@@ -261,8 +262,13 @@ def configs_report(sq, torch):
         big = N * K > 128 << 20
         Wc = [Wq] + ([Wq.clone() for _ in range(2)] if big else [])
         Xc = [X] + ([X.clone() for _ in range(2)] if T * K * X.element_size() > 128 << 20 else [])
-        t_q = _time_calls(torch, lambda x_: sq.sq_quant_act(x_, s, Xq=Xq, x_scale=xs), Xc)
-        t_g = _time_calls(torch, lambda wq: sq.sq_w8a8_gemm(Xq, xs, wq, ws, out_dtype=ydt, Y=Y), Wc)
+        # 7 batches of 20 calls each; median, 10th and 90th percentile of the
+        # per-call means
+        qs = [_time_calls(torch, lambda x_: sq.sq_quant_act(x_, s, Xq=Xq, x_scale=xs), Xc) for _ in range(7)]
+        gs = [_time_calls(torch, lambda wq: sq.sq_w8a8_gemm(Xq, xs, wq, ws, out_dtype=ydt, Y=Y), Wc)
+              for _ in range(7)]
+        t_q, t_g = float(np.median(qs)), float(np.median(gs))
+        pct = lambda v: [round(float(np.percentile(v, q)) * 1e3, 2) for q in (10, 50, 90)]
         ops = 2.0 * T * N * K
         gb = _gemm_bytes(T, N, K, 2 if ydt == torch.bfloat16 else 4)
         qb = _quant_bytes(T, K, X.element_size())
@@ -274,7 +280,8 @@ def configs_report(sq, torch):
                           "gemm_frac_hbm": gb / (t_g * 1e-3) / 1e9 / PEAK_HBM_GBS,
                           "quant_us": t_q * 1e3, "quant_GB/s": qb / (t_q * 1e-3) / 1e9,
                           "quant_frac_hbm": qb / (t_q * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                          "copies_rotated": len(Wc)}), flush=True)
+                          "gemm_us_p10_p50_p90": pct(gs), "quant_us_p10_p50_p90": pct(qs),
+                          "batches": "7 x 20 calls", "copies_rotated": len(Wc)}), flush=True)
         del X, Xs, Wq, Xq, Y, Wc, Xc
         torch.cuda.empty_cache()
 
