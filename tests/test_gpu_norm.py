@@ -70,7 +70,9 @@ def _check(sq, X, dtype, kind, g, b, eps, Xd=None):
     return Xq, xs
 
 
-SHAPES = [(1, 8), (37, 80), (37, 83), (300, 1000), (64, 4096), (33, 16384), (5, 20000)]
+# (800, 2056) and (1537, 2048): more rows than workgroups (3 per CU), so each
+# workgroup walks several rows and its last prefetch re-reads row R - 1
+SHAPES = [(1, 8), (37, 80), (37, 83), (300, 1000), (64, 4096), (33, 16384), (5, 20000), (800, 2056), (1537, 2048)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -133,7 +133,11 @@ def test_smooth_scales_full_range(sq):
 
 
 # ------------------------------------------------------------------ quantisers
-QSHAPES = [(1, 8), (37, 80), (5, 83), (64, 4096), (17, 16384), (3, 20000), (300, 1032), (2, 1)]
+# (800, 2056) and (1537, 2048): more rows than the row quantiser's 3 workgroups
+# per CU (768 on 256 CUs), so workgroups walk 2-3 rows and their last prefetch
+# past the final row re-reads row R - 1
+QSHAPES = [(1, 8), (37, 80), (5, 83), (64, 4096), (17, 16384), (3, 20000), (300, 1032), (2, 1), (800, 2056),
+           (1537, 2048)]
 
 
 def _special_rows(X):
