@@ -362,7 +362,8 @@ sq_status sq_w8a8_gemm(const int8_t *Xq, const float *x_scale,
                        hipStream_t stream);
 
 /* Bytes of device workspace sq_w8a8_linear needs for T tokens of width K
- * (the int8 codes and the per-token scales, each 256-byte aligned). */
+ * (the int8 codes and the per-token scales, each 256-byte aligned); 0 when
+ * T or K is below 1, SIZE_MAX when the size does not fit a size_t. */
 size_t sq_w8a8_linear_workspace_size(int64_t T, int64_t K);
 
 /*

@@ -130,6 +130,9 @@ def test_workspace(lib):
     assert lib.sq_w8a8_linear_workspace_size(0, 4) == 0
     assert lib.sq_w8a8_linear_workspace_size(3, 100) == 512 + 256
     assert lib.sq_w8a8_linear_workspace_size(8192, 8192) == 8192 * 8192 + 8192 * 4
+    # a product past size_t is reported as SIZE_MAX, not wrapped
+    assert lib.sq_w8a8_linear_workspace_size(1 << 62, 8192) == 2 ** 64 - 1
+    assert lib.sq_w8a8_linear_workspace_size(1 << 62, 1) == 2 ** 64 - 1
     need = lib.sq_w8a8_linear_workspace_size(16, 64)
     assert lib.sq_w8a8_linear(FAKE, F32, None, FAKE, FAKE, 16, 4, 64, FAKE, F32, FAKE, need - 1,
                               None) == SQ_ERR_WORKSPACE
@@ -205,4 +208,7 @@ def test_noalloc_arguments(lib):
     # 8192 x 8192 codes (64 MiB) and one token past 32 MiB of codes
     assert f(FAKE, BF16, None, FAKE, FAKE, 8192, 8192, 8192, FAKE, BF16, None) == SQ_ERR_SCRATCH
     assert f(FAKE, BF16, None, FAKE, FAKE, 4097, 4, 8192, FAKE, BF16, None) == SQ_ERR_SCRATCH
+    # T * K past 2^64 must not wrap into the scratch size
+    assert f(FAKE, BF16, None, FAKE, FAKE, (1 << 63) - 1, 4, 8192, FAKE, BF16, None) == SQ_ERR_SCRATCH
+    assert f(FAKE, BF16, None, FAKE, FAKE, 1 << 51, 4, 8192, FAKE, BF16, None) == SQ_ERR_SCRATCH
     assert b"SQ_ERR_SCRATCH" in lib.sq_status_string(SQ_ERR_SCRATCH)

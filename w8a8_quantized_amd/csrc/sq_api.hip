@@ -340,6 +340,10 @@ sq_status sq_w8a8_gemm(const int8_t* Xq, const float* x_scale, const int8_t* Wq,
 
 size_t sq_w8a8_linear_workspace_size(int64_t T, int64_t K) {
   if (T < 1 || K < 1) return 0;
+  // a size that does not fit size_t is reported as SIZE_MAX, which no
+  // workspace can satisfy (a wrapped product would pass the size check)
+  const size_t room = (SIZE_MAX - 1024) / 2;
+  if ((uint64_t)T > room / (uint64_t)K || (uint64_t)T > room / sizeof(float)) return SIZE_MAX;
   return round256((size_t)T * (size_t)K) + round256((size_t)T * sizeof(float));
 }
 
@@ -365,7 +369,7 @@ sq_status sq_w8a8_linear_noalloc(const void* X, sq_dtype x_t, const float* s, co
   if (!X || !Wq || !w_scale || !Y) return SQ_ERR_NULL;
   if (!in_dtype(x_t) || !in_dtype(y_t)) return SQ_ERR_DTYPE;
   if (T < 1 || N < 1 || K < 1 || K > SQ_MAX_K) return SQ_ERR_SHAPE;
-  if ((uint64_t)T * (uint64_t)K > SQ_NOALLOC_SCRATCH_BYTES ||
+  if ((uint64_t)T > SQ_NOALLOC_SCRATCH_BYTES / (uint64_t)K ||
       sq_w8a8_linear_workspace_size(T, K) > SQ_NOALLOC_SCRATCH_BYTES)
     return SQ_ERR_SCRATCH;
   void* ws = scratch_ptr();
