@@ -1,7 +1,8 @@
 """SmoothQuant W8A8 linear layer on MI355X (gfx950): Python binding of libsq.so.
 
 The kernels and the C ABI live in csrc/ and include/sq.h; this package only
-marshals torch tensors into those calls.  Importing it loads the HIP library
+marshals torch tensors into those calls (prepared.py saves and loads the
+offline products).  Importing it loads the HIP library
 and fails if it has not been built.
 """
 from .sq import (SQ_BF16, SQ_F32, SQ_I32, SQ_MAX_K, EXPORTED, LIB_PATH,  # noqa: F401
@@ -13,3 +14,4 @@ from .sq import (SQ_BF16, SQ_F32, SQ_I32, SQ_MAX_K, EXPORTED, LIB_PATH,  # noqa:
                  sq_smooth_scales_from_absmax, sq_status_string, sq_w8a8_gemm, sq_w8a8_linear,
                  sq_w8a8_linear_workspace_size, sq_w8a8_linear_noalloc,
                  SQ_NOALLOC_SCRATCH_BYTES)
+from .prepared import load_prepared, save_prepared  # noqa: F401

@@ -17,6 +17,7 @@
 // epilogue reads four consecutive channels, or a wave's tokens, with one access.
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace sq {
 
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(256) void decomp_gather_kernel(const T* __restrict_
 
 hipError_t launch_decomp_select(const float* absmax, int64_t K, int64_t n_o, int32_t* idx, float* mask,
                                 hipStream_t st) {
+  SQ_TRACE("decomp_rank + decomp_index (outlier set: %lld of K %lld columns)", (long long)n_o, (long long)K);
   hipLaunchKernelGGL(decomp_rank_kernel, dim3((unsigned)((K + 63) / 64)), dim3(256), 0, st, absmax, K, n_o, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_o == 0) return e;
@@ -126,6 +128,8 @@ hipError_t launch_decomp_gather(const void* A, bool bf16, int64_t rows, int64_t 
   if (total == 0) return hipSuccess;
   int64_t g = (total + 255) / 256;
   if (g > 8LL * ncu) g = 8LL * ncu;
+  SQ_TRACE("decomp_gather (%s) %lld outlier columns of %lld rows, K %lld, grid %lld x 256 threads",
+           bf16 ? "bf16" : "f32", (long long)n_o, (long long)rows, (long long)K, (long long)g);
   if (bf16)
     hipLaunchKernelGGL(decomp_gather_kernel<uint16_t>, dim3((unsigned)g), dim3(256), 0, st,
                        static_cast<const uint16_t*>(A), rows, K, idx, n_o, out);

@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 #include "slices.h"
 
 namespace sq {
@@ -668,6 +669,11 @@ static void launch_out(int out, bool outl, dim3 grid, dim3 block, hipStream_t st
                        const float* xs, const int8_t* Wq, const float* ws, int T, int N, int K, void* Y,
                        int64_t ldy, int tiles_n, int tiles_t, const float* xo, int64_t ldxo, const float* wo,
                        int64_t ldwo, int n_o) {
+  SQ_TRACE("gemm_i8_mfma tile %dx%d (channels x tokens) k-stage %d B, waves %dx%d, %d stages, out %s%s%s%s, "
+           "T %d N %d K %d, %dx%d tiles, grid %u x %u threads",
+           BN, BT, BK, WN, WT, ST, out == kOutF32 ? "f32" : out == kOutBF16 ? "bf16" : "i32",
+           outl ? ", outlier term" : "", F8 ? ", fp8" : "", PERSIST ? ", persistent" : "", T, N, K, tiles_n,
+           tiles_t, grid.x, block.x);
 #define SQ_GEMM_LAUNCH(O, L, F)                                                                                  \
   hipLaunchKernelGGL((gemm_i8_mfma_kernel<BN, BT, BK, WN, WT, ST, O, VEC, L, F, PERSIST>), grid, block, 0, st, Xq, \
                      xs, Wq, ws, T, N, K, Y, ldy, tiles_n, tiles_t, xo, ldxo, wo, ldwo, n_o)
@@ -875,6 +881,8 @@ hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st) {
   if (a.f8) {
     int64_t g = (a.T * a.N + 255) / 256;
     if (g > 65536) g = 65536;
+    SQ_TRACE("gemm_fp8_generic (scalar; K %% 16 != 0 or unaligned operands) T %lld N %lld K %lld, grid %lld x 256 threads",
+             (long long)a.T, (long long)a.N, (long long)a.K, (long long)g);
     const uint8_t* xq = reinterpret_cast<const uint8_t*>(a.Xq);
     const uint8_t* wq = reinterpret_cast<const uint8_t*>(a.Wq);
     if (a.out == kOutF32)
@@ -887,6 +895,8 @@ hipError_t launch_gemm_generic(const GemmArgs& a, hipStream_t st) {
   int64_t g = (total + 255) / 256;
   if (g > 65536) g = 65536;
   dim3 grid((unsigned)g), block(256);
+  SQ_TRACE("gemm_generic (scalar; K %% 16 != 0 or unaligned operands) T %lld N %lld K %lld, grid %lld x 256 threads",
+           (long long)a.T, (long long)a.N, (long long)a.K, (long long)g);
   switch (a.out) {
     case kOutF32:
       hipLaunchKernelGGL(gemm_generic_kernel<kOutF32>, grid, block, 0, st, a.Xq, a.xs, a.Wq, a.ws, a.T, a.N, a.K, a.Y,

@@ -32,6 +32,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 #include "slices.h"
 
 namespace sq {
@@ -423,6 +424,11 @@ static hipError_t gemv_cfg(const GemmArgs& a, hipStream_t st) {
     const size_t dyn = (size_t)n_o * 16 * (TB + NB) * sizeof(float);
     const int stage = (outl && dyn <= kGemvOutlierLds) ? 1 : 0;
     const size_t shm = stage ? dyn : 0;
+    SQ_TRACE("gemv_i8_mfma %d channels x %d tokens per workgroup, %d k-split waves, out %s%s%s, T %d N %d K %d, "
+             "grid %u x %u threads",
+             16 * NB, 16 * TB, KW, a.out == kOutF32 ? "f32" : a.out == kOutBF16 ? "bf16" : "i32",
+             outl ? (stage ? ", outlier term (LDS)" : ", outlier term") : "", F8 ? ", fp8" : "", T, N, K, grid.x,
+             block.x);
 #define SQ_GEMV_LAUNCH(O, L)                                                                             \
   hipLaunchKernelGGL((gemv_i8_mfma_kernel<NB, TB, O, KW, L, F8>), grid, block, shm, st, a.Xq, a.xs, Wq, ws, T, N, \
                      K, Y, a.N, vs, a.xo, a.T, wo, a.N, n_o, stage)

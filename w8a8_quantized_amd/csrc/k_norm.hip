@@ -29,6 +29,7 @@
 // Slow path: one workgroup per row, re-reading the row for each pass.
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace sq {
 
@@ -271,6 +272,9 @@ static hipError_t norm_fast(const T* A, int64_t R, int64_t K, const float* g, co
   const bool full = K == (int64_t)c2 * 2048;
   const int64_t g0 = R < 3LL * ncu ? R : 3LL * ncu;
   const dim3 grid((unsigned)g0), block(256);
+  SQ_TRACE("norm_quant_rows (%s%s, %s) %d chunks of 8 per thread%s, R %lld K %lld, grid %lld x 256 threads",
+           LAYER ? "LayerNorm" : "RMSNorm", HAS_B ? " with bias" : "", sizeof(T) == 2 ? "bf16" : "f32", c2,
+           full ? ", full rows" : "", (long long)R, (long long)K, (long long)g0);
 #define SQ_NORM_LAUNCH(C)                                                                                  \
   if (full) hipLaunchKernelGGL((norm_quant_rows_kernel<T, LAYER, HAS_B, C, true>), grid, block, 0, st, A, R, K, g, b, eps, Q, sc, mean, rstd); \
   else hipLaunchKernelGGL((norm_quant_rows_kernel<T, LAYER, HAS_B, C, false>), grid, block, 0, st, A, R, K, g, b, eps, Q, sc, mean, rstd);
@@ -294,6 +298,9 @@ static hipError_t norm_dispatch(const T* A, bool layer, int64_t R, int64_t K, co
              : norm_fast<T, true, false>(A, R, K, g, nullptr, eps, Q, sc, mean, rstd, ncu, st);
   }
   const int64_t g0 = R < 8LL * ncu ? R : 8LL * ncu;
+  SQ_TRACE("norm_quant_rows_slow (%s, %s; K %% 8 != 0, unaligned rows or K > %lld) R %lld K %lld, grid %lld x 256 threads",
+           layer ? "LayerNorm" : "RMSNorm", sizeof(T) == 2 ? "bf16" : "f32", (long long)kQuantFastMaxK, (long long)R,
+           (long long)K, (long long)g0);
   if (layer)
     hipLaunchKernelGGL((norm_quant_rows_slow_kernel<T, true>), dim3((unsigned)g0), dim3(256), 0, st, A, R, K, g, b, eps, Q, sc, mean, rstd);
   else
@@ -316,6 +323,7 @@ __global__ void fold_gain_kernel(const float* __restrict__ v, const float* __res
 }
 
 hipError_t launch_fold_gain(const float* v, const float* s, int64_t K, float* out, hipStream_t st) {
+  SQ_TRACE("fold_gain K %lld", (long long)K);
   hipLaunchKernelGGL(fold_gain_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, v, s, K, out);
   return hipGetLastError();
 }

@@ -41,6 +41,7 @@
 // row with plain IEEE binary32 divisions; identical results.
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace sq {
 
@@ -86,6 +87,9 @@ __device__ __forceinline__ void static_scale(const float* clip, float& scale, do
   scale = c == 0.0f ? 1.0f : c / (float)kQmax;
   rscale = c == 0.0f ? 0.0 : 1.0 / (double)scale;
 }
+
+constexpr const char* kQuantModeName[3] = {"activations, per-row range", "multiply by s, per-row range",
+                                           "activations, given range"};
 
 // MODE: 0 = activations, per-row range (divide by s); 1 = weights, per-row range
 // (multiply by s); 2 = activations, given range *clip (divide by s).
@@ -277,6 +281,9 @@ static hipError_t quant_fast(const T* A, int64_t R, int64_t K, const float* s, c
   dim3 grid((unsigned)g), block(256);
   const int c2 = cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8;   // instantiated sizes
   const bool full = K == (int64_t)c2 * 2048;
+  SQ_TRACE("quant_rows (%s%s%s, %s) %d chunks of 8 per thread%s, R %lld K %lld, grid %lld x 256 threads",
+           kQuantModeName[MODE], HAS_S ? ", smoothing" : "", F8 ? ", fp8" : "", sizeof(T) == 2 ? "bf16" : "f32", c2,
+           full ? ", full rows" : "", (long long)R, (long long)K, (long long)g);
 #define SQ_QUANT_LAUNCH(C)                                                                              \
   if (full) hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, true, F8, NTS>), grid, block, 0, st, A, R, K, s, clip, Q, scale); \
   else hipLaunchKernelGGL((quant_rows_kernel<T, MODE, HAS_S, C, false, F8, NTS>), grid, block, 0, st, A, R, K, s, clip, Q, scale);
@@ -298,6 +305,9 @@ static hipError_t quant_dispatch(const T* A, int64_t R, int64_t K, const float* 
              : quant_fast<T, MODE, false, F8, NTS>(A, R, K, s, clip, Q, scale, ncu, st);
   }
   int64_t g = R < 8LL * ncu ? R : 8LL * ncu;
+  SQ_TRACE("quant_rows_slow (%s%s%s, %s; K %% 8 != 0, unaligned rows or K > %lld) R %lld K %lld, grid %lld x 256 threads",
+           kQuantModeName[MODE], s ? ", smoothing" : "", F8 ? ", fp8" : "", sizeof(T) == 2 ? "bf16" : "f32",
+           (long long)kQuantFastMaxK, (long long)R, (long long)K, (long long)g);
   hipLaunchKernelGGL((quant_rows_slow_kernel<T, MODE, F8>), dim3((unsigned)g), dim3(256), 0, st, A, R, K,
                      s, clip, Q, scale);
   return hipGetLastError();

@@ -13,6 +13,7 @@
 // smoothing factors are here too.
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace sq {
 
@@ -426,11 +427,13 @@ static int grid_1d(int64_t n, int threads, int cap) {
 }
 
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
+  SQ_TRACE("fill %lld floats with %g", (long long)n, (double)v);
   hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_1d(n, 256, 1024)), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 
 hipError_t launch_fill2(float* p, float* q, int64_t n, float v, hipStream_t st) {
+  SQ_TRACE("fill 2 x %lld floats with %g", (long long)n, (double)v);
   hipLaunchKernelGGL(fill2_f32_kernel, dim3(grid_1d(n, 256, 1024)), dim3(256), 0, st, p, q, n, v);
   return hipGetLastError();
 }
@@ -448,6 +451,9 @@ static hipError_t col_absmax_t(const T* A, int64_t rows, int64_t cols, float* am
   if (slabs > 65535) slabs = 65535;
   int64_t slab = (rows + slabs - 1) / slabs;
   slabs = (rows + slab - 1) / slab;
+  SQ_TRACE("col_absmax (%s, %d elements per load, %d rows in flight) rows %lld cols %lld, grid %lld x %lld slabs of %lld rows",
+           sizeof(T) == 2 ? "bf16" : "f32", VEC, U, (long long)rows, (long long)cols, (long long)gx, (long long)slabs,
+           (long long)slab);
   hipLaunchKernelGGL((col_absmax_kernel<T, VEC, U>), dim3((unsigned)gx, (unsigned)slabs), dim3(256), 0,
                      st, A, rows, cols, slab, amax);
   return hipGetLastError();
@@ -465,6 +471,10 @@ static hipError_t col_absmax_pair_t(const void* X, int64_t T, const void* W, int
     return S;
   };
   const int64_t SX = interleave(bx / (bx + bw), cbX, T), SW = interleave(bw / (bx + bw), cbW, N);
+  SQ_TRACE("col_absmax_pair (X %s T %lld: %lld column blocks x %lld row interleave; W %s N %lld: %lld x %lld) K %lld, "
+           "grid %lld x 256 threads",
+           sizeof(TX) == 2 ? "bf16" : "f32", (long long)T, (long long)cbX, (long long)SX, sizeof(TW) == 2 ? "bf16" : "f32",
+           (long long)N, (long long)cbW, (long long)SW, (long long)K, (long long)(cbX * SX + cbW * SW));
   hipLaunchKernelGGL((col_absmax_pair_kernel<TX, TW, 8>), dim3((unsigned)(cbX * SX + cbW * SW)), dim3(256), 0, st,
                      static_cast<const TX*>(X), T, cbX, SX, static_cast<const TW*>(W), N, cbW, SW, K, xa, wa);
   return hipGetLastError();
@@ -494,6 +504,8 @@ hipError_t launch_col_absmax(const void* A, bool bf16, int64_t rows, int64_t col
     if (S < 1) S = 1;
     if (S > rows) S = rows;
     if (S > 65535) S = 65535;
+    SQ_TRACE("col_absmax_blk (f32, 4 KB column blocks) rows %lld cols %lld, grid %lld blocks x %lld row interleave",
+             (long long)rows, (long long)cols, (long long)cb, (long long)S);
     hipLaunchKernelGGL((col_absmax_blk_kernel<float, 8>), dim3((unsigned)cb, (unsigned)S), dim3(256), 0,
                        st, a, rows, cols, amax);
     return hipGetLastError();
@@ -514,6 +526,8 @@ static hipError_t tensor_absmax_t(const T* A, int64_t rows, int64_t cols, const 
   int64_t slab = (rows + slabs - 1) / slabs;
   slabs = (rows + slab - 1) / slab;
   const dim3 grid((unsigned)gx, (unsigned)slabs), block(256);
+  SQ_TRACE("tensor_absmax (%s, slab form, %d elements per load) rows %lld cols %lld, grid %lld x %lld slabs",
+           sizeof(T) == 2 ? "bf16" : "f32", VEC, (long long)rows, (long long)cols, (long long)gx, (long long)slabs);
   if (s) hipLaunchKernelGGL((tensor_absmax_kernel<T, VEC, U, true>), grid, block, 0, st, A, rows, cols, slab, s, amax);
   else hipLaunchKernelGGL((tensor_absmax_kernel<T, VEC, U, false>), grid, block, 0, st, A, rows, cols, slab, s, amax);
   return hipGetLastError();
@@ -531,6 +545,8 @@ static hipError_t tensor_absmax_rows_t(const T* A, int64_t R, int64_t K, const f
   int64_t g = (R + U - 1) / U;
   const int64_t cap = (sizeof(T) == 2 ? 1 : 2) * (int64_t)ncu;
   if (g > cap) g = cap;
+  SQ_TRACE("tensor_absmax_rows (%s, %d chunks of 8 per thread, %d rows per group) R %lld K %lld, grid %lld x 256 threads",
+           sizeof(T) == 2 ? "bf16" : "f32", CPT, U, (long long)R, (long long)K, (long long)g);
   if (K == (int64_t)CPT * 2048)
     hipLaunchKernelGGL((tensor_absmax_rows_kernel<T, HAS_S, CPT, U, true>), dim3((unsigned)g), dim3(256), 0, st, A, R, K, s, amax);
   else
@@ -568,6 +584,8 @@ hipError_t launch_tensor_absmax(const void* A, bool bf16, int64_t rows, int64_t 
 template <typename T>
 static hipError_t smooth_from_w_t(const T* W, int64_t N, int64_t K, const float* xa, double alpha, float* s,
                                   bool vec_ok, hipStream_t st) {
+  SQ_TRACE("smooth_w%s (%s, weight column maxima and factors in one pass) N %lld K %lld, alpha %g",
+           vec_ok ? "strip" : "col", sizeof(T) == 2 ? "bf16" : "f32", (long long)N, (long long)K, alpha);
   if (vec_ok) {
     constexpr int SC = 8 * (16 / sizeof(T));
     hipLaunchKernelGGL((smooth_wstrip_kernel<T, 4>), dim3((unsigned)((K + SC - 1) / SC)), dim3(256), 0, st, W, N,
@@ -587,6 +605,7 @@ hipError_t launch_smooth_scales_from_w(const void* W, bool bf16, int64_t N, int6
 
 hipError_t launch_smooth_scales(const float* xa, const float* wa, int64_t K, float alpha, float* s,
                                 hipStream_t st) {
+  SQ_TRACE("smooth_scales K %lld, alpha %g", (long long)K, (double)alpha);
   hipLaunchKernelGGL(smooth_scales_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, xa,
                      wa, K, (double)alpha, s);
   return hipGetLastError();
