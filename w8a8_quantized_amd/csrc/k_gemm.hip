@@ -13,8 +13,9 @@
 // operand a 32-row block of Xq (rows = tokens); a lane then ends up holding four
 // consecutive output channels of one token, which the epilogue stages through
 // LDS and writes as whole row segments.  Tiles of Wq and Xq are staged through an
-// LDS ring of 2 (large problems) or 4 (small, latency-bound problems) K stages,
-// one barrier per stage; the 16-byte chunk position within each LDS row is
+// LDS ring of two K stages (three for the 64x128 tile), 128 bytes wide for the
+// tiles with 256 rows and the 64x128 tile, 256 bytes for the 64x64 and 128x128
+// tiles, one barrier per stage; the 16-byte chunk position within each LDS row is
 // XOR-swizzled by the row index so that both the staging writes and the fragment
 // reads (32 rows, same column) are free of bank conflicts.  Workgroups are
 // remapped so that each XCD (which owns a private L2) works through a contiguous
@@ -140,7 +141,8 @@ constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 1
 // slot l of the instruction's 1 KB block, so each lane fetches the logical
 // chunk that belongs at its slot under the XOR swizzle).  Fragments of step q+1
 // are read from LDS while the MFMAs of step q run; the per-stage barrier sits
-// after half of the last step's MFMAs.  The barrier is a bare s_barrier
+// after all (16-wave tile) or half (the others) of the last step's MFMAs.  The
+// barrier is a bare s_barrier
 // preceded by this wave's own "vmcnt <= loads of later stages" wait: a fenced
 // barrier would also wait for the later stages still in flight.
 //
