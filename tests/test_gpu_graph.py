@@ -66,6 +66,29 @@ def test_linear_graph_replays(sq, T, N, K):
         assert np.array_equal(host(Y_g), host(want)), f"replay {r}"
 
 
+@pytest.mark.parametrize("T,N,K", [(300, 384, 512), (16, 512, 1024)])
+def test_noalloc_linear_graph_replays(sq, T, N, K):
+    """sq_w8a8_linear_noalloc, the entry point for callers that cannot allocate
+    (its workspace is the library's fixed per-GPU scratch): captured, replayed
+    with new inputs, each replay equal to the workspace call."""
+    rng = np.random.default_rng(7 * T + N + K)
+    w = WL.page_tiny_fixture(seed=13, T=T, N=N, K=K)
+    W = torch.from_numpy(w.W).to(DEV)
+    s, _, _ = sq.sq_smooth_scales(_draw(rng, T, K), W, 0.5)
+    Wq, ws = sq.sq_quantize_weights(W, s)
+    X_in = _draw(rng, T, K)
+    Y_g = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    g = _capture(lambda: sq.sq_w8a8_linear_noalloc(X_in, s, Wq, ws, Y_g))
+    for r in range(4):
+        X = _draw(rng, T, K, scale=1.0 + r)
+        X_in.copy_(X)
+        g.replay()
+        torch.cuda.synchronize()
+        want = sq.sq_w8a8_linear(X, s, Wq, ws)   # eager, caller workspace
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y_g), host(want)), f"replay {r}"
+
+
 def test_smooth_scales_graph_replays(sq):
     """The statistics pass: zero fill, fused column maxima, factors."""
     rng = np.random.default_rng(3)
