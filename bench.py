@@ -136,10 +136,13 @@ def cpu_baseline(w, target_s=20.0, runs=3):
                       f"{', '.join(f'{d:.1f}' for d in walls)} s wall"}
 
 
-def decode_measure(sq, torch, reps=30):
+def decode_measure(sq, torch, reps=30, placements=3):
     """Decode-shaped GEMM rate: 3 copies of the int8 weights (3 x 235 MB, more
     than the 256 MB Infinity Cache) used in turn; `reps` launches back to back
-    between two events."""
+    between two events.  The rate depends on where the weights land in memory
+    (fresh allocations of the same copies differ by up to ~17%), so the copies
+    are allocated `placements` times and the median is reported, with every
+    value."""
     import workloads as WL
     w = WL.make("decode_t16_k8192_n28672")
     dev = torch.device("cuda")
@@ -150,9 +153,7 @@ def decode_measure(sq, torch, reps=30):
     Wq, ws = sq.sq_quantize_weights(W, s)
     Wq8, ws8 = sq.sq_quantize_weights_fp8(W, s)
     del W
-    torch.cuda.empty_cache()    # each copy in an allocation of its own
-    copies = [Wq] + [Wq.clone() for _ in range(2)]
-    copies8 = [Wq8] + [Wq8.clone() for _ in range(2)]
+    torch.cuda.empty_cache()
     Xq, xs = sq.sq_quant_act(X, s)
     Xq8, xs8 = sq.sq_quant_act_fp8(X, s)
     Y = torch.empty((w.T, w.N), dtype=torch.bfloat16, device=dev)
@@ -170,13 +171,24 @@ def decode_measure(sq, torch, reps=30):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    ms = per_launch(lambda wq: sq.sq_w8a8_gemm(Xq, xs, wq, ws, Y=Y), copies)
-    ms8 = per_launch(lambda wq: sq.sq_fp8_gemm(Xq8, xs8, wq, ws8, Y=Y), copies8)
+    runs, runs8, held = [], [], []
+    for _ in range(placements):
+        copies = [Wq.clone() for _ in range(3)]       # each copy in an allocation of its own
+        copies8 = [Wq8.clone() for _ in range(3)]
+        runs.append(per_launch(lambda wq: sq.sq_w8a8_gemm(Xq, xs, wq, ws, Y=Y), copies))
+        runs8.append(per_launch(lambda wq: sq.sq_fp8_gemm(Xq8, xs8, wq, ws8, Y=Y), copies8))
+        held.append((copies, copies8))                 # kept, so the next set lands elsewhere
+    ms, ms8 = float(np.median(runs)), float(np.median(runs8))
     byts = _gemm_bytes(w.T, w.N, w.K, 2)
     gbs, gbs8 = byts / (ms * 1e-3) / 1e9, byts / (ms8 * 1e-3) / 1e9
+    del held
+    torch.cuda.empty_cache()
     return {"workload": w.name, "T": w.T, "N": w.N, "K": w.K, "us": ms * 1e3, "GB/s": gbs,
             "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": byts, "weight_copies_rotated": 3,
-            "fp8": {"us": ms8 * 1e3, "GB/s": gbs8, "frac_hbm": gbs8 / PEAK_HBM_GBS}}
+            "us_per_placement": [round(x * 1e3, 2) for x in runs],
+            "placements": f"median over {placements} allocations of the three weight copies",
+            "fp8": {"us": ms8 * 1e3, "GB/s": gbs8, "frac_hbm": gbs8 / PEAK_HBM_GBS,
+                    "us_per_placement": [round(x * 1e3, 2) for x in runs8]}}
 
 
 def _time_calls(torch, fn, copies, reps=20):
