@@ -148,6 +148,8 @@ def _narrow_codes(rng, r, k):
 @pytest.mark.parametrize("T,N,K", SHAPES + [(300, 520, 112), (1000, 4100, 336), (100, 12800, 208),
                                             (128, 16384, 336), (768, 16384, 208), (200, 24576, 336),
                                             (2100, 8200, 336),
+                                            # 1 KB-segment decode form
+                                            (16, 16390, 8192), (3, 16384, 12288),
                                             # the five workload shapes, in the bench's configuration
                                             (128, 1024, 1024), (512, 4096, 4096), (16, 28672, 8192),
                                             (2048, 16384, 4096), (8192, 8192, 8192)])

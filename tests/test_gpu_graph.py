@@ -44,7 +44,7 @@ def _draw(rng, T, K, scale=1.0):
     return torch.from_numpy(X).to(torch.bfloat16).to(DEV)
 
 
-@pytest.mark.parametrize("T,N,K", [(300, 384, 512), (16, 512, 1024)])
+@pytest.mark.parametrize("T,N,K", [(300, 384, 512), (16, 512, 1024), (16, 16448, 8192)])
 def test_linear_graph_replays(sq, T, N, K):
     """sq_w8a8_linear (quantiser + GEMM, or the decode GEMM at T <= 32)."""
     rng = np.random.default_rng(T + N + K)
@@ -141,10 +141,10 @@ def test_decomp_gemm_graph_replays(sq):
         assert np.array_equal(host(Y_g), host(want)), f"replay {r}"
 
 
-@pytest.mark.parametrize("T,N,K", [(2100, 8200, 208), (300, 520, 336), (16, 640, 512)])
+@pytest.mark.parametrize("T,N,K", [(2100, 8200, 208), (300, 520, 336), (16, 640, 512), (16, 16448, 8192)])
 def test_fp8_gemm_graph_replays(sq, T, N, K):
-    """sq_fp8_gemm (persistent 256x256 form, 64x64 tiles, decode kernel) with its
-    FP8 operands copied into the captured buffers before each replay."""
+    """sq_fp8_gemm (persistent 256x256 form, 64x64 tiles, both decode forms) with
+    its FP8 operands copied into the captured buffers before each replay."""
     rng = np.random.default_rng(T + N + K)
     W = torch.from_numpy((rng.standard_normal((N, K)) * 0.05).astype(np.float32)).to(DEV)
     Wq, ws = sq.sq_quantize_weights_fp8(W)

@@ -208,6 +208,9 @@ GEMM_SHAPES = [
     (64, 300, 528), (48, 28672, 80), (33, 136, 12288), (64, 72, 12304), (40, 4100, 1040), (64, 6200, 528),
     (20, 6200, 272), (9, 8200, 272), (24, 9000, 400), (20, 8180, 272), (33, 8192, 208), (48, 10240, 208), (16, 12300, 96),
     (3, 8192, 16384), (20, 6200, 16400), (40, 8192, 16384), (5, 12300, 8192), (16, 16000, 8208),
+    # decode kernel, 1 KB-segment form (<= 16 tokens, >= 64 channels per CU, K a
+    # multiple of 4096 from 8192): ragged channel tail, 1 and 9 tokens, 3 segments per wave
+    (16, 16390, 8192), (1, 16384, 12288), (9, 16448, 8192),
     # prefill kernel, 64x64 tiles (< 256 tiles of 128x128; 256-byte K stages), ragged
     # edges and K tails; one, two, three and more stages
     (65, 40, 16), (100, 129, 64), (300, 1000, 80), (100, 129, 304), (65, 40, 688), (257, 513, 1040),
@@ -256,6 +259,8 @@ def test_decode_shapes_assume_256_cus(sq):
                                    # waves (K >= 16384, 6144 <= N <= 8192); 32 channels
                                    # with 2 waves (N = 8192, 17-64 tokens)
                                    (5, 12300, 8192), (16, 16000, 8208), (3, 8192, 16384),
+                                   # 1 KB-segment decode form, ragged and whole
+                                   (16, 16390, 8192), (7, 16448, 12288),
                                    (40, 8192, 16384), (20, 6200, 16400), (33, 8192, 208),
                                    (70, 33, 83), (64, 130, 64), (129, 257, 64), (1000, 4100, 272),
                                    (100, 129, 688), (1000, 4100, 608), (2100, 8200, 336),

@@ -51,6 +51,23 @@ def test_trace_lines(sq, capfd):
     assert "T 300 N 512 K 1024" in lines[1] and "out bf16" in lines[1]
     assert "T 16 N 1024 K 2048" in lines[3]
     assert "R 300 K 1024" in lines[0] and "R 16 K 2048" in lines[2]
+    # the 1 KB-segment decode form: wide layer, K a multiple of 4096
+    wide = _layer(sq, 16, 16384, 8192, rng)
+    torch.cuda.synchronize()
+    capfd.readouterr()
+    os.environ["SQ_TRACE"] = "1"
+    try:
+        sq.sq_w8a8_linear(*wide)
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err.splitlines()
+    finally:
+        if old is None:
+            del os.environ["SQ_TRACE"]
+        else:
+            os.environ["SQ_TRACE"] = old
+    lines = [l for l in err if l.startswith("sq: ")]
+    assert [l.split()[1] for l in lines] == ["quant_rows", "gemv_seg_i8_mfma"], lines
+    assert "T 16 N 16384 K 8192" in lines[1]
     # switched off again: no lines
     X, s, Wq, ws = prefill
     sq.sq_w8a8_linear(X, s, Wq, ws)

@@ -27,6 +27,9 @@
 // position XOR-swizzled by row so that the 16 rows of one read hit distinct banks.
 // The token codes are operand B (16 tokens per MFMA).  Integer accumulation is
 // exact; the epilogue is y = fl32(fl32(acc) * fl32(x_scale[t] * w_scale[n])).
+//
+// A second form, gemv_seg_kernel, serves wide layers with deep K at up to 16
+// tokens: each load instruction reads 1 KB of one weight row, see its comment.
 #include <type_traits>
 #include <utility>
 
@@ -402,6 +405,214 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 #endif
 }
 
+// Decode form for wide layers with deep K: up to 16 tokens, no outlier term.
+// Every weight load instruction reads 1 KB of one row (64 lanes x 16 bytes), so
+// a wave's reads are whole kilobyte runs of the rows.  The time of such reads
+// did not depend on where the weight pages landed, unlike the 256-byte row
+// pieces of gemv_i8_mfma_kernel: 16 x 28672 x 8192 took 41.1-42.3 us on every
+// one of several fresh allocations, against 37.8-45.8 us.  A workgroup owns 64
+// channels (four 16-channel blocks) and four waves, which take alternate 1 KB
+// segments of K.  For one segment a wave keeps the 16 tokens' codes in
+// registers and streams its four channel blocks through a single register slot.
+// A block's 16 loaded rows are written to the wave's LDS tile, whose row pitch
+// is 1040 bytes so that an MFMA read of 16 rows hits distinct banks.  The next
+// block's loads are issued, and then the block's 16 k-steps run from LDS.  So
+// one block's loads (16 KB per wave) are in flight while the previous block is
+// multiplied.  The partial sums of the four waves are added exactly (int32) or
+// in wave order (FP8, binary32) through LDS; the epilogue is that of
+// gemv_i8_mfma_kernel.  Requires T <= 16, K % 16 == 0, (N + 64) * K <= 2^31 and
+// T * K < 2^31 (the host slices N), and 16-byte aligned Xq and Wq.
+template <int OUT, bool F8>
+__global__ __launch_bounds__(256) void gemv_seg_kernel(const int8_t* __restrict__ Xq, const float* __restrict__ xs,
+                                                       const int8_t* __restrict__ Wq, const float* __restrict__ ws,
+                                                       int T, int N, int K, void* __restrict__ Y, int64_t ldy,
+                                                       int vec_store) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NB = 4, KW = 4;           // channel blocks per workgroup, K-split waves
+  constexpr int SEG = 1024;               // K bytes per segment
+  constexpr int ROWB = SEG + 16;          // LDS row pitch
+  constexpr int TILE = 16 * ROWB;         // one wave's tile: 16 rows of a segment
+  constexpr int KS = SEG / 64;            // MFMA k-steps per segment (16)
+  constexpr int kOob = 0x7FFFFFF0;        // offset the range check turns into zeros
+  constexpr int kWaitLoads = 0x0F70;      // s_waitcnt vmcnt(0), other counters free
+  __shared__ __attribute__((aligned(16))) int8_t lds_all[KW * TILE];
+  static_assert((KW - 1) * NB * 64 * 16 <= KW * TILE, "partial sums must fit the LDS tiles");
+  const int lane = threadIdx.x & 63, kw = threadIdx.x >> 6;
+  int8_t* tile = lds_all + kw * TILE;
+  const int n0 = blockIdx.x * 16 * NB;
+  const __amdgpu_buffer_rsrc_t rsW = gemv_rsrc(Wq, N * K);   // rows >= N read as zeros
+  const __amdgpu_buffer_rsrc_t rsX = gemv_rsrc(Xq, T * K);   // tokens >= T read as zeros
+  const int fi = lane & 15, fg = lane >> 4;
+  // this wave's segments: kw, kw + KW, ...; unit u = (segment u / NB, block u % NB)
+  const int nall = (K + SEG - 1) / SEG;
+  const int nseg = nall > kw ? (nall - kw + KW - 1) / KW : 0;
+  const int U = nseg * NB;
+
+  // epilogue scale factors, fetched before the K loop (see gemv_i8_mfma_kernel)
+  float xsv = 0.0f, wsv[NB][4];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wsv[i][e] = 0.0f;
+  if (OUT != kOutI32 && kw == 0) {
+    if (fi < T) xsv = xs[fi];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n0 + i * 16 + 4 * fg + e < N) wsv[i][e] = ws[n0 + i * 16 + 4 * fg + e];
+  }
+
+  // rows n0 + 16 b .. +15 of unit u's segment: row r is one instruction, lane ->
+  // bytes lane*16 .. +15 of the segment (cache policy 2: non-temporal)
+  v4i wr[16];
+  auto load_rows = [&](int u) {
+    const int j = u / NB, b = u - j * NB;
+    const int k0 = (j * KW + kw) * SEG + lane * 16;
+    const bool in = u < U && k0 < K;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wr[r] = __builtin_amdgcn_raw_buffer_load_b128(rsW, in ? (n0 + b * 16 + r) * K + k0 : kOob, 0, 2);
+  };
+  // token codes of segment j in operand-B layout: token fi, k-step m, piece fg
+  v4i tok[KS];
+  auto load_tokens = [&](int j) {
+    const int kb = (j * KW + kw) * SEG + fg * 16;
+    const bool in = j < nseg;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) {
+      const int k = kb + m * 64;
+      tok[m] = __builtin_amdgcn_raw_buffer_load_b128(rsX, (in && k < K) ? fi * K + k : kOob, 0, 0);
+    }
+  };
+
+  using AccT = std::conditional_t<F8, v4f, v4i>;
+  AccT acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = AccT{0, 0, 0, 0};
+
+  auto unit = [&](auto b_c, int u) {
+    constexpr int b = decltype(b_c)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitLoads);   // this unit's rows (and tokens) have arrived
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) *reinterpret_cast<v4i*>(tile + r * ROWB + lane * 16) = wr[r];
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows(u + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int8_t* L = tile + fi * ROWB + fg * 16;
+    if constexpr (F8) {
+      // the two 16-byte pieces of k-steps m and m + 1, for weights and tokens alike
+#pragma unroll
+      for (int m = 0; m < KS; m += 2) {
+        const v8i wv = __builtin_shufflevector(*reinterpret_cast<const v4i*>(L + m * 64),
+                                               *reinterpret_cast<const v4i*>(L + (m + 1) * 64), 0, 1, 2, 3, 4, 5,
+                                               6, 7);
+        const v8i x8 = __builtin_shufflevector(tok[m], tok[m + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, x8, acc[b], 0, 0, 0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KS; ++m)
+        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const v4i*>(L + m * 64), tok[m], acc[b],
+                                                       0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (b == NB - 1) load_tokens(u / NB + 1);   // after the segment's last block
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  load_rows(0);
+  load_tokens(0);
+  for (int u = 0; u < U; u += NB)
+    static_for(std::make_integer_sequence<int, NB>{}, [&](auto b) { unit(b, u + decltype(b)::value); });
+  // the loads issued past the last unit read zeros; let them land before the
+  // LDS tiles are reused
+  __builtin_amdgcn_s_waitcnt(kWaitLoads);
+  __syncthreads();
+  AccT* red = reinterpret_cast<AccT*>(lds_all);
+  if (kw > 0) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) red[((kw - 1) * NB + i) * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (kw > 0) return;
+#pragma unroll
+  for (int w = 1; w < KW; ++w)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc[i] += red[((w - 1) * NB + i) * 64 + lane];
+
+  // epilogue: lane holds n = n0 + i*16 + 4*fg + 0..3 for token t = fi
+  const int t = fi;
+  if (t >= T) return;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = n0 + i * 16 + 4 * fg;
+    if (n >= N) continue;
+    const int nrem = N - n;
+    const bool vec = vec_store && nrem >= 4;
+    const AccT a4 = acc[i];
+    if (OUT == kOutI32) {
+      int* y = static_cast<int*>(Y) + (int64_t)t * ldy + n;
+      if (vec) *reinterpret_cast<int4*>(y) = make_int4(a4[0], a4[1], a4[2], a4[3]);
+      else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = a4[e];
+      continue;
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (xsv * wsv[i][e]) : 0.0f;
+    if (OUT == kOutF32) {
+      float* y = static_cast<float*>(Y) + (int64_t)t * ldy + n;
+      if (vec) *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
+      else for (int e = 0; e < 4 && e < nrem; ++e) y[e] = v[e];
+    } else {
+      uint16_t* y = static_cast<uint16_t*>(Y) + (int64_t)t * ldy + n;
+      if (vec) {
+        uint2 pk;
+        pk.x = f32x2_to_bf16x2(v[0], v[1]);
+        pk.y = f32x2_to_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(y) = pk;
+      } else {
+        for (int e = 0; e < 4 && e < nrem; ++e) y[e] = (uint16_t)f32_to_bf16(v[e]);
+      }
+    }
+  }
+#endif
+}
+
+template <bool F8>
+static hipError_t gemv_seg_cfg(const GemmArgs& a, hipStream_t st) {
+  // split N so that one launch's weight slice spans < 2^31 bytes (32-bit offsets)
+  const int64_t n_chunk = rows_per_slice(a.K, 64);
+  const size_t osz = a.out == kOutBF16 ? 2 : 4;
+  for (int64_t nb = 0; nb < a.N; nb += n_chunk) {
+    const int N = (int)(a.N - nb < n_chunk ? a.N - nb : n_chunk);
+    dim3 grid((N + 63) / 64), block(256);
+    const int8_t* Wq = a.Wq + nb * a.K;
+    const float* ws = a.ws ? a.ws + nb : nullptr;
+    void* Y = static_cast<char*>(a.Y) + nb * osz;
+    const int vs = (a.vec_store && nb % 4 == 0) ? 1 : 0;
+    const int T = (int)a.T, K = (int)a.K;
+    SQ_TRACE("gemv_seg_i8_mfma 64 channels per workgroup, 4 k-split waves over 1 KB segments, out %s%s, "
+             "T %d N %d K %d, grid %u x %u threads",
+             a.out == kOutF32 ? "f32" : a.out == kOutBF16 ? "bf16" : "i32", F8 ? ", fp8" : "", T, N, K, grid.x,
+             block.x);
+#define SQ_SEG_LAUNCH(O) \
+  hipLaunchKernelGGL((gemv_seg_kernel<O, F8>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs)
+    if constexpr (F8) {   // float outputs only (the ABI rejects int32 for FP8)
+      if (a.out == kOutF32) SQ_SEG_LAUNCH(kOutF32); else SQ_SEG_LAUNCH(kOutBF16);
+    } else {
+      if (a.out == kOutF32) SQ_SEG_LAUNCH(kOutF32);
+      else if (a.out == kOutBF16) SQ_SEG_LAUNCH(kOutBF16);
+      else SQ_SEG_LAUNCH(kOutI32);
+    }
+#undef SQ_SEG_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 constexpr size_t kGemvOutlierLds = 64 * 1024;
 
 template <int NB, int TB, int KW, bool F8>
@@ -481,6 +692,18 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // against 95.3 us (32 channels), 6144 x 4096 at 64 tokens 14.3 against 19.9 us.
   const bool outl = a.n_o > 0 && a.out != kOutI32;
   const int64_t c64 = (a.N + 63) / 64, c32 = (a.N + 31) / 32;
+  // At least one 64-channel block per CU, up to 16 tokens, K a multiple of 4096
+  // from 8192 up: the 1 KB-segment form (gemv_seg_kernel), whose four waves then
+  // take equal shares of K.  Measured over one allocation of the weights each,
+  // against the form below: 16384 x 8192 26.4 against 28.2 us, 28672 x 8192 41.8
+  // against 43.5 (1 token 39.9 against 42.7), 24576 x 12288 55.8 against 60.9,
+  // 49152 x 12288 94.2 against 126.8, 16384 x 16384 at 8 tokens 47.5 against
+  // 62.2, 57344 x 8192 at 1 token 75.8 against 86.5.  It lost where the waves'
+  // shares differ (16384 x 9216 29.5 against 26.3 us, 16384 x 14336 41.6 against
+  // 39.5) and where each wave has a single segment, leaving nothing to overlap
+  // (16384 x 5120 20.5 against 15.9).
+  if (a.T <= 16 && !outl && c64 >= ncu && a.K >= 8192 && a.K % 4096 == 0)
+    return a.f8 ? gemv_seg_cfg<true>(a, st) : gemv_seg_cfg<false>(a, st);
   // Layers of 3/4 to one 64-channel block per CU, K >= 8192, up to 16 tokens:
   // 8 waves (12288 x 12288 at 1/16 tokens 27.6/30.0 against 32.2/33.7 us,
   // 12288 x 49152 94.4/103.2 against 105.3/112.3; at 28672 channels 8 waves lost)
