@@ -95,12 +95,14 @@ def test_decomp_layer(sq, xdt, T, N, K, n_o, out):
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("T,N,K,n_o", [(100, 96, 512, 90), (100, 96, 512, 110), (2048, 2048, 256, 120),
-                                       (4096, 4096, 128, 26), (4096, 4096, 128, 30)])
+                                       (4096, 4096, 128, 26), (4096, 4096, 128, 30),
+                                       (16, 16390, 8192, 41), (5, 16384, 12288, 48), (9, 16448, 8192, 49)])
 def test_decomp_gemm_outlier_staging(sq, T, N, K, n_o, out):
     """Prefill tiles copy their outlier operands into LDS when they fit (64x64
     tiles up to ~90 outliers, 128x128 up to ~94-107, 256x256 up to 26) and read
-    them from global memory otherwise: outlier counts on both sides of those
-    limits, outputs in full."""
+    them from global memory otherwise; the 1 KB-segment decode form takes up to
+    48 outliers (staged in LDS), more go to the other decode form: outlier counts
+    on both sides of those limits, outputs in full."""
     rng = np.random.default_rng(T + N + K + n_o)
     X = rng.standard_normal((T, K)).astype(np.float32)
     X[:, rng.choice(K, n_o, replace=False)] *= 25

@@ -422,11 +422,21 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 // in wave order (FP8, binary32) through LDS; the epilogue is that of
 // gemv_i8_mfma_kernel.  Requires T <= 16, K % 16 == 0, (N + 64) * K <= 2^31 and
 // T * K < 2^31 (the host slices N), and 16-byte aligned Xq and Wq.
-template <int OUT, bool F8>
+// OUTL: the epilogue adds the decomposition's outlier-channel product (as in
+// gemv_i8_mfma_kernel, same order and roundings).  The workgroup's operands,
+// xo[o][t < 16] and wo[o][n0 .. n0 + 64), are copied into dynamic LDS before
+// the K loop, at most kSegOutlierLoads loads per thread, so the host sends at
+// most kSegMaxOutliers outliers here; each wave forms the sums of one channel
+// block after the K loop.
+constexpr int kSegOutlierLoads = 16;
+constexpr int kSegMaxOutliers = 48;   // 48 x 320 B + 66.5 KB: two workgroups per CU
+static_assert(kSegMaxOutliers * (16 + 64) <= kSegOutlierLoads * 256, "one batch of staging loads");
+template <int OUT, bool OUTL, bool F8>
 __global__ __launch_bounds__(256) void gemv_seg_kernel(const int8_t* __restrict__ Xq, const float* __restrict__ xs,
                                                        const int8_t* __restrict__ Wq, const float* __restrict__ ws,
                                                        int T, int N, int K, void* __restrict__ Y, int64_t ldy,
-                                                       int vec_store) {
+                                                       int vec_store, const float* __restrict__ xo, int64_t ldxo,
+                                                       const float* __restrict__ wo, int64_t ldwo, int n_o) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NB = 4, KW = 4;           // channel blocks per workgroup, K-split waves
   constexpr int SEG = 1024;               // K bytes per segment
@@ -436,7 +446,9 @@ __global__ __launch_bounds__(256) void gemv_seg_kernel(const int8_t* __restrict_
   constexpr int kOob = 0x7FFFFFF0;        // offset the range check turns into zeros
   constexpr int kWaitLoads = 0x0F70;      // s_waitcnt vmcnt(0), other counters free
   __shared__ __attribute__((aligned(16))) int8_t lds_all[KW * TILE];
-  static_assert((KW - 1) * NB * 64 * 16 <= KW * TILE, "partial sums must fit the LDS tiles");
+  static_assert((KW - 1) * NB * 64 * 16 + (KW - 1) * 64 * 16 <= KW * TILE,
+                "partial and outlier sums must fit the LDS tiles");
+  static_assert(!(F8 && (OUTL || OUT == kOutI32)), "FP8: float outputs, no outlier term");
   const int lane = threadIdx.x & 63, kw = threadIdx.x >> 6;
   int8_t* tile = lds_all + kw * TILE;
   const int n0 = blockIdx.x * 16 * NB;
@@ -522,18 +534,63 @@ __global__ __launch_bounds__(256) void gemv_seg_kernel(const int8_t* __restrict_
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // outlier operands: entries [0, nx) are ox[o][t], then ow[o][c]
+  constexpr int TL = 16, CL = 16 * NB;
+  extern __shared__ __attribute__((aligned(16))) float seg_outl[];
+  float* ox = seg_outl;
+  float* ow = seg_outl + n_o * TL;
+  const int nx = n_o * TL, ntot = nx + n_o * CL;
+  float sv[kSegOutlierLoads];
+  if constexpr (OUTL) {
+#pragma unroll
+    for (int u = 0; u < kSegOutlierLoads; ++u) {
+      const int q = threadIdx.x + u * 256;
+      float v = 0.0f;
+      if (q < nx) {
+        const int o = q / TL, tl = q - o * TL;
+        if (tl < T) v = xo[(int64_t)o * ldxo + tl];
+      } else if (q < ntot) {
+        const int o = (q - nx) / CL, c = q - nx - o * CL;
+        if (n0 + c < N) v = wo[(int64_t)o * ldwo + n0 + c];
+      }
+      sv[u] = v;
+    }
+  }
   load_rows(0);
   load_tokens(0);
+  if constexpr (OUTL) {   // stored while the first rows are in flight
+#pragma unroll
+    for (int u = 0; u < kSegOutlierLoads; ++u) {
+      const int q = threadIdx.x + u * 256;
+      if (q < ntot) seg_outl[q] = sv[u];
+    }
+  }
   for (int u = 0; u < U; u += NB)
     static_for(std::make_integer_sequence<int, NB>{}, [&](auto b) { unit(b, u + decltype(b)::value); });
   // the loads issued past the last unit read zeros; let them land before the
-  // LDS tiles are reused
+  // LDS tiles are reused (the barrier also publishes the staged outlier operands)
   __builtin_amdgcn_s_waitcnt(kWaitLoads);
   __syncthreads();
   AccT* red = reinterpret_cast<AccT*>(lds_all);
+  float4* sor = reinterpret_cast<float4*>(red + (KW - 1) * NB * 64);
   if (kw > 0) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) red[((kw - 1) * NB + i) * 64 + lane] = acc[i];
+  }
+  // outlier-channel sums (gemv_outlier_sums): wave kw forms those of block kw
+  float so[NB][1][4];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) so[i][0][e] = 0.0f;
+  if constexpr (OUTL) {
+    static_for(std::make_integer_sequence<int, NB>{}, [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (kw == i) {
+        gemv_outlier_sums<NB, 1, i, i + 1>(so, n_o, 1, ox, ow, xo, ldxo, wo, ldwo, T, N, n0, fi, fg);
+        if (i > 0) sor[(i - 1) * 64 + lane] = make_float4(so[i][0][0], so[i][0][1], so[i][0][2], so[i][0][3]);
+      }
+    });
   }
   __syncthreads();
   if (kw > 0) return;
@@ -541,6 +598,13 @@ __global__ __launch_bounds__(256) void gemv_seg_kernel(const int8_t* __restrict_
   for (int w = 1; w < KW; ++w)
 #pragma unroll
     for (int i = 0; i < NB; ++i) acc[i] += red[((w - 1) * NB + i) * 64 + lane];
+  if constexpr (OUTL) {
+#pragma unroll
+    for (int i = 1; i < NB; ++i) {
+      const float4 f = sor[(i - 1) * 64 + lane];
+      so[i][0][0] = f.x; so[i][0][1] = f.y; so[i][0][2] = f.z; so[i][0][3] = f.w;
+    }
+  }
 
   // epilogue: lane holds n = n0 + i*16 + 4*fg + 0..3 for token t = fi
   const int t = fi;
@@ -561,6 +625,10 @@ __global__ __launch_bounds__(256) void gemv_seg_kernel(const int8_t* __restrict_
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (e < nrem) ? (float)a4[e] * (xsv * wsv[i][e]) : 0.0f;
+    if (OUTL) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = v[e] + so[i][0][e];
+    }
     if (OUT == kOutF32) {
       float* y = static_cast<float*>(Y) + (int64_t)t * ldy + n;
       if (vec) *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
@@ -593,18 +661,24 @@ static hipError_t gemv_seg_cfg(const GemmArgs& a, hipStream_t st) {
     void* Y = static_cast<char*>(a.Y) + nb * osz;
     const int vs = (a.vec_store && nb % 4 == 0) ? 1 : 0;
     const int T = (int)a.T, K = (int)a.K;
-    SQ_TRACE("gemv_seg_i8_mfma 64 channels per workgroup, 4 k-split waves over 1 KB segments, out %s%s, "
+    const bool outl = a.n_o > 0 && a.out != kOutI32;
+    if (outl && (F8 || a.n_o > kSegMaxOutliers)) return hipErrorInvalidValue;
+    const float* wo = outl ? a.wo + nb : nullptr;
+    const int n_o = outl ? (int)a.n_o : 0;
+    const size_t shm = (size_t)n_o * (16 + 64) * sizeof(float);
+    SQ_TRACE("gemv_seg_i8_mfma 64 channels per workgroup, 4 k-split waves over 1 KB segments, out %s%s%s, "
              "T %d N %d K %d, grid %u x %u threads",
-             a.out == kOutF32 ? "f32" : a.out == kOutBF16 ? "bf16" : "i32", F8 ? ", fp8" : "", T, N, K, grid.x,
-             block.x);
-#define SQ_SEG_LAUNCH(O) \
-  hipLaunchKernelGGL((gemv_seg_kernel<O, F8>), grid, block, 0, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs)
+             a.out == kOutF32 ? "f32" : a.out == kOutBF16 ? "bf16" : "i32", outl ? ", outlier term (LDS)" : "",
+             F8 ? ", fp8" : "", T, N, K, grid.x, block.x);
+#define SQ_SEG_LAUNCH(O, L)                                                                                   \
+  hipLaunchKernelGGL((gemv_seg_kernel<O, L, F8>), grid, block, shm, st, a.Xq, a.xs, Wq, ws, T, N, K, Y, a.N, vs, \
+                     a.xo, a.T, wo, a.N, n_o)
     if constexpr (F8) {   // float outputs only (the ABI rejects int32 for FP8)
-      if (a.out == kOutF32) SQ_SEG_LAUNCH(kOutF32); else SQ_SEG_LAUNCH(kOutBF16);
+      if (a.out == kOutF32) SQ_SEG_LAUNCH(kOutF32, false); else SQ_SEG_LAUNCH(kOutBF16, false);
     } else {
-      if (a.out == kOutF32) SQ_SEG_LAUNCH(kOutF32);
-      else if (a.out == kOutBF16) SQ_SEG_LAUNCH(kOutBF16);
-      else SQ_SEG_LAUNCH(kOutI32);
+      if (a.out == kOutF32) { if (outl) SQ_SEG_LAUNCH(kOutF32, true); else SQ_SEG_LAUNCH(kOutF32, false); }
+      else if (a.out == kOutBF16) { if (outl) SQ_SEG_LAUNCH(kOutBF16, true); else SQ_SEG_LAUNCH(kOutBF16, false); }
+      else SQ_SEG_LAUNCH(kOutI32, false);
     }
 #undef SQ_SEG_LAUNCH
     hipError_t e = hipGetLastError();
@@ -701,8 +775,10 @@ hipError_t launch_gemv_mfma(const GemmArgs& a, int ncu, hipStream_t st) {
   // 62.2, 57344 x 8192 at 1 token 75.8 against 86.5.  It lost where the waves'
   // shares differ (16384 x 9216 29.5 against 26.3 us, 16384 x 14336 41.6 against
   // 39.5) and where each wave has a single segment, leaving nothing to overlap
-  // (16384 x 5120 20.5 against 15.9).
-  if (a.T <= 16 && !outl && c64 >= ncu && a.K >= 8192 && a.K % 4096 == 0)
+  // (16384 x 5120 20.5 against 15.9).  With the decomposition's outlier term up
+  // to kSegMaxOutliers outliers (operands staged in LDS at two workgroups per CU).
+  if (a.T <= 16 && c64 >= ncu && a.K >= 8192 && a.K % 4096 == 0 &&
+      (!outl || (!a.f8 && a.n_o <= kSegMaxOutliers)))
     return a.f8 ? gemv_seg_cfg<true>(a, st) : gemv_seg_cfg<false>(a, st);
   // Layers of 3/4 to one 64-channel block per CU, K >= 8192, up to 16 tokens:
   // 8 waves (12288 x 12288 at 1/16 tokens 27.6/30.0 against 32.2/33.7 us,
