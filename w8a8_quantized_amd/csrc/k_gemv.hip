@@ -409,13 +409,13 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 #endif
 }
 
-// Decode form for wide layers with deep K: up to 16 tokens, no outlier term.
-// Every weight load instruction reads 1 KB of one row (64 lanes x 16 bytes), so
-// a wave's reads are whole kilobyte runs of the rows.  The time of such reads
-// did not depend on where the weight pages landed, unlike the 256-byte row
-// pieces of gemv_i8_mfma_kernel: 16 x 28672 x 8192 took 41.1-42.3 us on every
-// one of several fresh allocations, against 37.8-45.8 us.  A workgroup owns 64
-// channels (four 16-channel blocks) and four waves, which take alternate 1 KB
+// Decode form for wide layers with deep K, up to 16 tokens.  Every weight load
+// instruction reads 1 KB of one row (64 lanes x 16 bytes), so a wave's reads are
+// whole kilobyte runs of the rows.  The time of such reads did not depend on
+// where the weight pages landed, unlike the 256-byte row pieces of
+// gemv_i8_mfma_kernel (16 x 28672 x 8192: this form 39.8-40.3 us on each of three
+// fresh allocations in one run, the other 37.8-45.8 us over several).  A workgroup owns
+// 64 channels (four 16-channel blocks) and four waves, which take alternate 1 KB
 // segments of K.  For one segment a wave keeps the 16 tokens' codes in
 // registers and streams its four channel blocks through a single register slot.
 // A block's 16 loaded rows are written to the wave's LDS tile, whose row pitch
@@ -424,10 +424,11 @@ __global__ __launch_bounds__(64 * KW) void gemv_i8_mfma_kernel(
 // once with the same half of the next block.  Then the block's 16 k-steps run
 // from LDS.  So 8 to 16 rows per wave (8-16 KB) are always in flight; waiting
 // for all 16 rows before reloading any measured 5% slower (41.8-42.0 against
-// 39.8-40.0 us on 16 x 28672 x 8192).  The partial sums of the four waves are added exactly (int32) or
-// in wave order (FP8, binary32) through LDS; the epilogue is that of
-// gemv_i8_mfma_kernel.  Requires T <= 16, K % 16 == 0, (N + 64) * K <= 2^31 and
-// T * K < 2^31 (the host slices N), and 16-byte aligned Xq and Wq.
+// 39.8-40.0 us on 16 x 28672 x 8192).  The partial sums of the four waves are
+// added exactly (int32) or in wave order (FP8, binary32) through LDS; the
+// epilogue is that of gemv_i8_mfma_kernel.  Requires T <= 16, K % 16 == 0,
+// (N + 64) * K <= 2^31 and T * K < 2^31 (the host slices N), and 16-byte aligned
+// Xq and Wq.
 // OUTL: the epilogue adds the decomposition's outlier-channel product (as in
 // gemv_i8_mfma_kernel, same order and roundings).  The workgroup's operands,
 // xo[o][t < 16] and wo[o][n0 .. n0 + 64), are copied into dynamic LDS before
