@@ -113,7 +113,7 @@ def _check_gemm(sq, Xq_r, xs_r, Wq_r, ws_r, ti=None, ni=None):
     return float(ratio.max())
 
 
-@pytest.mark.parametrize("T,N,K", SHAPES)
+@pytest.mark.parametrize("T,N,K", SHAPES + [(9, 16390, 8192)])   # + the 1 KB-segment decode form, ragged
 def test_fp8_gemm_accuracy(sq, T, N, K):
     X, W, s = _case(3 * T + N + K, T, K, N, "f32")
     Xq_r, xs_r = O.quant_act_fp8(X, s)
