@@ -113,10 +113,11 @@ def test_smooth_scales_graph_replays(sq):
         assert np.array_equal(host(s), host(s_e)), f"replay {r}"
 
 
-def test_decomp_gemm_graph_replays(sq):
-    """The decode GEMM with the outlier term (dynamic LDS for the outlier operands)."""
+@pytest.mark.parametrize("T,N,K,n_o", [(16, 640, 512, 9), (16, 16448, 8192, 41)])
+def test_decomp_gemm_graph_replays(sq, T, N, K, n_o):
+    """The decode GEMM with the outlier term (dynamic LDS for the outlier
+    operands), in the 256-byte and the 1 KB-segment form."""
     rng = np.random.default_rng(5)
-    T, N, K, n_o = 16, 640, 512, 9
     W = torch.from_numpy((rng.standard_normal((N, K)) * 0.05).astype(np.float32)).to(DEV)
     a = torch.from_numpy(rng.uniform(0, 1, K).astype(np.float32)).to(DEV)
     idx, mask = sq.sq_decomp_select(a, n_o)
